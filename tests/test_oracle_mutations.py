@@ -1,0 +1,113 @@
+"""Plant plausible mistakes in copies of the oracle's attention core (CPU only) and check
+that the pins catch each of them: the pins are not vacuous."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import attention as A
+
+
+def _mutant(kind):
+    def attend_rows(q, k_of_head, v_of_head, key_pos, q_pos, window, scale, n_kv_heads):
+        q = np.asarray(q, dtype=np.float64)
+        q_len, hq, d = q.shape
+        G = hq // n_kv_heads
+        key_pos = np.asarray(key_pos)
+        q_pos = np.asarray(q_pos)
+        w_eff = window + 1 if (kind == "window_off_by_one" and window) else window
+        lo = np.array([A.key_bounds(int(p), w_eff)[0] for p in q_pos])
+        hi = q_pos - 1 if kind == "strict_causal" else q_pos
+        visible = (key_pos[None, :] >= lo[:, None]) & (key_pos[None, :] <= hi[:, None])
+        out = np.zeros((q_len, hq, d))
+        lse = np.full((q_len, hq), -np.inf)
+        sc = 1.0 if kind == "no_scale" else scale
+        for h in range(hq):
+            g = h % n_kv_heads if kind == "gqa_modulo" else h // G
+            Kg, Vg = k_of_head(g), v_of_head(g)
+            s = sc * (q[:, h, :] @ Kg.T)
+            s = np.where(visible, s, -np.inf)
+            m = s.max(axis=1)
+            has = np.isfinite(m)
+            w = np.exp(s - np.where(has, m, 0.0)[:, None])
+            l = w.sum(axis=1)
+            if kind == "no_normalise":
+                l = np.ones_like(l)
+            o = w @ Vg
+            out[has, h] = o[has] / l[has, None]
+            lse[has, h] = m[has] + np.log(l[has])
+        return out, lse
+    return attend_rows
+
+
+def _sdpa_pin(ctx=300, q_len=16, hq=8, hkv=2, d=16, window=64):
+    g = np.random.default_rng(1)
+    k, v = g.standard_normal((ctx, hkv, d)), g.standard_normal((ctx, hkv, d))
+    q = g.standard_normal((q_len, hq, d))
+    out, _ = oracle.attention_contiguous(q, k, v, ctx, window=window, dtype="f64")
+    G = hq // hkv
+    qt = torch.from_numpy(q).permute(1, 0, 2)[None]
+    kt = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(G, 0)[None]
+    vt = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(G, 0)[None]
+    qp, kp = torch.arange(ctx - q_len, ctx)[:, None], torch.arange(ctx)[None, :]
+    mask = (kp <= qp) & (kp > qp - window)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask)
+    return np.abs(out - ref[0].permute(1, 0, 2).numpy()).max() < 1e-12
+
+
+def _count_pin():
+    ctx = 2000
+    k = np.random.default_rng(2).standard_normal((ctx, 1, 4))
+    _, lse = oracle.attention_contiguous(np.zeros((16, 1, 4)), k, k, ctx, window=512, dtype="f64")
+    return bool(np.all(lse == math.log(512)))
+
+
+def _ring_pin():
+    from synth import ring_case
+    c = ring_case(77, 0, 30720, 16, 4, 2, 8, 2048, 512)
+    out, _ = oracle.attention_ring(c.q, c.k_ring, c.v_ring, c.pos0, c.ring_head, 2048, 512)
+    n = c.ctx_len
+    k = np.zeros((n, 2, 8), np.uint16)
+    v = np.zeros((n, 2, 8), np.uint16)
+    k[c.rows_first:], v[c.rows_first:] = c.k_rows, c.v_rows
+    ro, _ = oracle.attention_contiguous(c.q, k, v, n, window=512, dtype="bf16")
+    return np.abs(out - ro).max() < 1e-14
+
+
+def test_unmutated_oracle_passes_the_pins():
+    assert _sdpa_pin() and _count_pin() and _ring_pin()
+
+
+@pytest.mark.parametrize("kind", ["window_off_by_one", "strict_causal", "no_scale",
+                                  "gqa_modulo", "no_normalise"])
+def test_each_planted_mistake_is_caught(kind, monkeypatch):
+    monkeypatch.setattr(A, "attend_rows", _mutant(kind))
+    assert not (_sdpa_pin() and _count_pin())
+
+
+def test_planted_ring_slot_mistake_is_caught(monkeypatch):
+    real = A.gather_ring
+
+    def shifted(k_ring, v_ring, positions, ring_size, chunk=64):
+        return real(k_ring, v_ring, np.asarray(positions) + 1, ring_size, chunk)
+    monkeypatch.setattr(A, "gather_ring", shifted)
+    assert not _ring_pin()
+
+
+def test_planted_v_transpose_mistake_is_caught(monkeypatch):
+    from synth import paged_case
+
+    def wrong(k_pool, v_pool, page_table, positions, chunk=64):
+        positions = np.asarray(positions)
+        slot = np.asarray(page_table)[positions // chunk]
+        off = positions % chunk
+        # reads V as if it were stored key-major like K
+        return (lambda g: np.asarray(k_pool)[slot, g, off, :],
+                lambda g: np.asarray(v_pool).reshape(v_pool.shape[0], v_pool.shape[1], chunk, -1)[slot, g, off, :])
+    c = paged_case(78, 0, 500, 16, 4, 2, 64)
+    ref = oracle.attention_contiguous(c.q, c.k_rows, c.v_rows, 500, dtype="bf16")
+    monkeypatch.setattr(A, "gather_paged", wrong)
+    o, _ = oracle.attention_paged(c.q, c.k_pool, c.v_pool, c.page_table, 500)
+    assert not (np.abs(o - ref[0]).max() <= 1e-3)   # wrong values or NaN from unset slots
