@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Benchmark of the speculative-decoding verify step on one MI355X.
+
+A step is one pass of the whole verify hot path over one block of 16 drafted tokens:
+40 attention layers (three in four are 512-token sliding-window layers over a 2,048-slot
+position ring, every fourth a full-attention layer over a paged pool of 64-token chunks at
+context 131,072) and the greedy accept over [17 x 65536] logits.  Inputs are seeded synthetic
+data already resident in HBM; the step is captured once in a HIP graph and replayed.
+
+The JSON line also carries the per-layer figure at context 262,144 (one paged verify layer,
+both kernels), the roofline of the dominant kernel (the paged split-K attention kernel, timed
+live with HIP events on the stream it runs on), and the fp64 oracle timed on the host cores
+over a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload stack_40l_131k|paged_256k]
+    python bench.py --mode copy     # plain 1-GiB device copies, for HBM counter calibration
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KV GB/s (% of HBM peak) for 16-token verify attention; µs/layer at 256K"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_chunk_attn_paged_131k.json")
+KERNEL_SRC = os.path.join(ROOT, "ring_kv_amd", "csrc", "attn_chunked.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="stack_40l_131k",
+                    choices=["stack_40l_131k", "paged_256k"])
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy"])
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-256k", action="store_true", help="skip the 262,144-context layer")
+    return ap.parse_args()
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def event_ms(fn, n, torch):
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(n):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / n
+
+
+class Stack:
+    """Device-resident inputs, outputs and workspaces of the 40-layer verify step."""
+
+    def __init__(self, torch, rk, synth):
+        self.torch, self.rk = torch, rk
+        t = lambda a: rk.tensor_from_numpy(a, "cuda")  # noqa: E731
+        self.layers = []
+        self.kv_bytes = 0
+        for l in range(synth.STACK_LAYERS):
+            c, acc = synth.workload("stack_40l_131k", l, keep_rows=False)
+            d = dict(kind=c.kind, q=t(c.q), out=torch.empty((16, 16, 128), dtype=torch.float32, device="cuda"),
+                     lse=torch.empty((16, 16), dtype=torch.float32, device="cuda"))
+            if c.kind == "ring":
+                d.update(k=t(c.k_ring), v=t(c.v_ring), pos0=c.pos0, window=c.window)
+            else:
+                d.update(k=t(c.k_pool), v=t(c.v_pool), pt=t(c.page_table), ctx=c.ctx_len)
+            self.kv_bytes += c.kv_bytes
+            self.layers.append(d)
+            del c
+        self.accept = acc
+        self.logits = t(acc.logits)
+        self.prop = t(acc.proposals)
+        self.acc_len = torch.empty(1, dtype=torch.int32, device="cuda")
+        self.committed = torch.empty(17, dtype=torch.int32, device="cuda")
+        self.argmax = torch.empty(17, dtype=torch.int32, device="cuda")
+        self.accept_bytes = acc.logits.nbytes
+        L = rk.lib()
+        from ring_kv_amd._lib import AttnDims
+        import ctypes
+        dims = AttnDims(16, 16, 4, 128, 0.0, 1)
+        self.ws_paged = torch.empty(max(1, L.verify_attn_paged_workspace_bytes(ctypes.byref(dims), 131072, 64, 0)),
+                                    dtype=torch.uint8, device="cuda")
+        self.ws_ring = torch.empty(max(1, L.verify_attn_ring_workspace_bytes(ctypes.byref(dims), 2048, 512, 0)),
+                                   dtype=torch.uint8, device="cuda")
+        self.ws_acc = torch.empty(L.verify_accept_workspace_bytes(16, 65536), dtype=torch.uint8, device="cuda")
+        self.splits = rk.verify_attn_paged_auto_splits(16, 4, 128, 16, 131072)
+        self.part_o = torch.empty((4, self.splits, 64, 128), dtype=torch.float32, device="cuda")
+        self.part_l = torch.empty((4, self.splits, 64), dtype=torch.float32, device="cuda")
+
+    def step(self):
+        rk = self.rk
+        for d in self.layers:
+            if d["kind"] == "ring":
+                rk.verify_attn_ring(d["q"], d["k"], d["v"], d["pos0"], d["window"], out=d["out"],
+                                    lse=d["lse"], workspace=self.ws_ring)
+            else:
+                rk.verify_attn_paged(d["q"], d["k"], d["v"], d["pt"], d["ctx"], out=d["out"],
+                                     lse=d["lse"], workspace=self.ws_paged)
+        rk.verify_accept(self.logits, self.prop, accept_len=self.acc_len, committed=self.committed,
+                         row_argmax=self.argmax, workspace=self.ws_acc)
+
+    def paged_partial_round(self):
+        """The dominant kernel alone: the paged split-K kernel over each paged layer once."""
+        for d in self.layers:
+            if d["kind"] == "paged":
+                self.rk.verify_attn_paged_partial(d["q"], d["k"], d["v"], d["pt"], d["ctx"],
+                                                  self.splits, part_out=self.part_o,
+                                                  part_lse=self.part_l)
+
+
+def cpu_baseline(synth, oracle):
+    """The fp64 oracle on a bounded sample of the step: one paged layer at 131,072, three ring
+    layers and the accept, timed on the host cores."""
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    cases = [synth.workload("stack_40l_131k", l, keep_rows=False)[0] for l in (3, 0, 1, 2)]
+    acc = synth.workload("stack_40l_131k", 0, keep_rows=False)[1]
+    kv = sum(c.kv_bytes for c in cases)
+    t0 = time.perf_counter()
+    for c in cases:
+        if c.kind == "paged":
+            oracle.attention_paged(c.q, c.k_pool, c.v_pool, c.page_table, c.ctx_len)
+        else:
+            oracle.attention_ring(c.q, c.k_ring, c.v_ring, c.pos0, c.ring_head, c.ring_size, c.window)
+    oracle.greedy_accept(acc.logits, acc.proposals)
+    dt = time.perf_counter() - t0
+    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": "1 paged layer (ctx 131,072) + 3 ring layers + accept [17x65536] of the "
+                      "40-layer step; KV bytes of the sample / wall time"}
+
+
+def traffic_entry(per_launch_bytes):
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except Exception:  # noqa: BLE001
+        return None
+    if t.get("kernel_sha") != kernel_hash():
+        return None          # the kernel changed since the counters were taken
+    return t.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import ring_kv_amd as rk
+
+    rk.lib()   # fails loudly if the HIP library is not built
+
+    if args.mode == "copy":
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        ms = event_ms(lambda: b.copy_(a), 5, torch)
+        print(json.dumps({"mode": "copy", "bytes_per_copy": n, "ms_per_copy": ms,
+                          "gbps": 2 * n / ms / 1e6}), flush=True)
+        return
+
+    import synth
+
+    res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded N(0,1) bf16 K/V, planted-argmax logits)"}
+
+    if args.workload == "stack_40l_131k":
+        log("building the 40-layer step inputs")
+        st = Stack(torch, rk, synth)
+        step_bytes = st.kv_bytes + st.accept_bytes
+        for _ in range(args.warmup):
+            st.step()
+        torch.cuda.synchronize()
+        eager_ms = event_ms(st.step, max(1, args.steps // 2), torch)
+        log(f"eager step {eager_ms:.3f} ms")
+        ms = eager_ms
+        graph = False
+        if not args.no_graph:
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                st.step()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                st.step()
+            for _ in range(args.warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            ms = event_ms(g.replay, args.steps, torch)
+            graph = True
+            log(f"graph step {ms:.3f} ms")
+        # dominant kernel: paged split-K at 131,072, 10 launches per round
+        for _ in range(2):
+            st.paged_partial_round()
+        rounds = max(2, args.steps // 4)
+        k_ms = event_ms(st.paged_partial_round, rounds, torch) / 10
+        per_launch = 2 * 131072 * 4 * 128 * 2
+        achieved = per_launch / (k_ms * 1e-3) / 1e9
+        log(f"paged split kernel {k_ms * 1e3:.1f} us/launch, {achieved:.0f} GB/s")
+        res.update({
+            "value": round(step_bytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+            "ms_per_step": round(ms, 4), "eager_ms_per_step": round(eager_ms, 4),
+            "hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "config": {"workload": "stack_40l_131k", "layers": 40, "ring_layers": 30,
+                       "paged_layers": 10, "q_len": 16, "n_q_heads": 16, "n_kv_heads": 4,
+                       "head_dim": 128, "ring_size": 2048, "window": 512, "paged_ctx": 131072,
+                       "chunk": 64, "vocab": 65536, "hip_graph": graph,
+                       "kv_bytes_per_step": st.kv_bytes, "logit_bytes_per_step": st.accept_bytes},
+            "roofline": {"bound": "hbm", "kernel": "chunk_attn_kernel (paged, split-K) at 131,072",
+                         "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                         "us_per_launch": round(k_ms * 1e3, 2),
+                         "algorithmic_bytes_per_launch": per_launch,
+                         "traffic": traffic_entry(per_launch)},
+        })
+        del st
+        torch.cuda.empty_cache()
+
+    if args.workload == "paged_256k" or not args.no_256k:
+        log("building the 262,144-context layer")
+        c, _ = synth.workload("paged_256k", keep_rows=False)
+        t = lambda a: rk.tensor_from_numpy(a, "cuda")  # noqa: E731
+        q, kp, vp, pt = t(c.q), t(c.k_pool), t(c.v_pool), t(c.page_table)
+        kv = c.kv_bytes
+        del c
+        out = torch.empty((16, 16, 128), dtype=torch.float32, device="cuda")
+        lse = torch.empty((16, 16), dtype=torch.float32, device="cuda")
+        splits = rk.verify_attn_paged_auto_splits(16, 4, 128, 16, 262144)
+        po = torch.empty((4, splits, 64, 128), dtype=torch.float32, device="cuda")
+        pl = torch.empty((4, splits, 64), dtype=torch.float32, device="cuda")
+        fn = lambda: rk.verify_attn_paged(q, kp, vp, pt, 262144, out=out, lse=lse)  # noqa: E731
+        part = lambda: rk.verify_attn_paged_partial(q, kp, vp, pt, 262144, splits,  # noqa: E731
+                                                    part_out=po, part_lse=pl)
+        for _ in range(max(2, args.warmup)):
+            fn()
+        n = max(5, args.steps)
+        us = event_ms(fn, n, torch) * 1e3
+        us_split = event_ms(part, n, torch) * 1e3
+        log(f"256K layer {us:.1f} us (split kernel {us_split:.1f} us)")
+        res.update({"us_per_layer_256k": round(us, 2),
+                    "kv_gbps_256k": round(kv / (us * 1e-6) / 1e9, 1),
+                    "hbm_frac_256k": round(kv / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                    "split_kernel_us_256k": round(us_split, 2)})
+        if args.workload == "paged_256k":
+            res.update({"value": res["kv_gbps_256k"], "unit": "GB/s", "ms_per_step": round(us / 1e3, 5),
+                        "config": {"workload": "paged_256k", "ctx": 262144, "q_len": 16,
+                                   "n_q_heads": 16, "n_kv_heads": 4, "head_dim": 128,
+                                   "chunk": 64, "splits": splits},
+                        "roofline": {"bound": "hbm", "kernel": "chunk_attn_kernel (paged, split-K) at 262,144",
+                                     "achieved": round(kv / (us_split * 1e-6) / 1e9, 1),
+                                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                     "frac": round(kv / (us_split * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                                     "us_per_launch": round(us_split, 2),
+                                     "algorithmic_bytes_per_launch": kv, "traffic": None}})
+        del q, kp, vp, pt
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        import oracle
+        log("cpu baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline(synth, oracle)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

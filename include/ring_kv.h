@@ -1,0 +1,226 @@
+/*
+ * ring_kv.h -- C interface of libring_kv, the speculative-decoding verify step on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (lucebox post "Laguna XS 2.1 33B on a RTX 3090: 296 tok/s peak, 152 tok/s
+ * at 256K context"):
+ *   - a drafter proposes a block of tokens that the target checks in one batched
+ *     forward ("The model, fast MoE with a drafter in the box");
+ *   - sliding-window layers attend a position ring, slot = pos mod 2048, window 512
+ *     ("3. Ring caches for the sliding-window layers");
+ *   - full-attention layers attend a GPU pool of 64-token chunks ("Three
+ *     optimizations", item 1, KVFlash paging), found through a page table;
+ *   - only tokens the target itself would emit are committed: the longest agreeing
+ *     drafted prefix plus the target's next token ("TL;DR"; "The model, fast MoE with
+ *     a drafter in the box").
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Memory.  Every tensor pointer is a DEVICE pointer owned by the caller (the library
+ *   never allocates, frees, or keeps a pointer after the call returns).  Scratch
+ *   memory is passed in as `workspace`; query its size with the matching
+ *   *_workspace_bytes() function.
+ * Streams.  `stream` is a hipStream_t (NULL: the default stream).  Calls enqueue
+ *   kernels and return without synchronising; the caller keeps every buffer alive
+ *   until the stream has passed the work.
+ * Errors.  Every call returns an rkv_status.  All shape, dtype, pointer and size
+ *   checks run on the host before any HIP call, so a rejected call touches no
+ *   device state.  A failed launch returns RKV_ERR_HIP.  No C++ exception crosses
+ *   this interface.
+ * Determinism.  Identical inputs give bit-identical outputs: no float atomics, a
+ *   fixed reduction order, and paged work ordered by logical chunk (never by
+ *   physical slot), so permuting the pool changes nothing.
+ *
+ * Attention definition (every layout).  Query i of the block (0 <= i < q_len) sits at
+ * absolute position p_i; query head h reads KV head g = h / G, G = n_q_heads /
+ * n_kv_heads.  It attends keys j with lo_i <= j <= p_i, where lo_i = 0 (full
+ * causal) or max(0, p_i - window + 1) (a window of `window` keys including its own
+ * position).  With s_j = scale * <Q[i][h], K(j)[g]>:
+ *     out[i][h][:] = sum_j exp(s_j - m) V(j)[g][:] / sum_j exp(s_j - m),  m = max_j s_j
+ *     lse[i][h]    = m + ln sum_j exp(s_j - m)            (natural log)
+ * Query i sees the block's earlier tokens and itself, so row i equals single-token
+ * decoding at context p_i + 1.
+ *
+ * Layouts (row-major, innermost last)
+ *   Q                 [q_len][n_q_heads][head_dim]           bf16 or f32
+ *   contiguous K, V   [ctx_len][n_kv_heads][head_dim]        same dtype as Q
+ *   chunked K store   [n_slots][n_kv_heads][64][head_dim]    bf16   (key-major chunk)
+ *   chunked V store   [n_slots][n_kv_heads][head_dim][64]    bf16   (dimension-major chunk)
+ *   out               [q_len][n_q_heads][head_dim]           f32
+ *   lse               [q_len][n_q_heads]                     f32 (may be NULL)
+ * A chunked store holds 64 consecutive positions per slot.  The paged pool puts
+ * logical chunk c = j / 64 in slot page_table[c]; the ring is a store of
+ * ring_size / 64 slots that puts position j at ring slot j mod ring_size, i.e. chunk
+ * slot (j mod ring_size) / 64, offset j mod 64.  V is kept dimension-major inside a
+ * chunk so that the PV product streams it without a transpose.
+ */
+#ifndef RING_KV_H
+#define RING_KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RKV_ABI_VERSION 1
+#define RKV_CHUNK 64            /* positions per chunk slot */
+#define RKV_MAX_ROWS 256        /* q_len * (n_q_heads / n_kv_heads) limit */
+
+typedef enum rkv_status {
+  RKV_OK = 0,
+  RKV_ERR_NULL = -1,        /* a required pointer is NULL */
+  RKV_ERR_SHAPE = -2,       /* head counts, head_dim, q_len or ctx_len out of range */
+  RKV_ERR_DTYPE = -3,       /* dtype not supported by this call */
+  RKV_ERR_RING = -4,        /* ring too small for window + block, ring_size not a multiple of
+                               64, or ring_head is not pos0 mod ring_size */
+  RKV_ERR_TABLE = -5,       /* chunk_size is not 64, or the page table / pool is too small */
+  RKV_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than *_workspace_bytes() */
+  RKV_ERR_HIP = -7,         /* a HIP launch failed */
+  RKV_ERR_ARG = -8          /* another argument out of range (window, splits, sizes) */
+} rkv_status;
+
+typedef enum rkv_dtype { RKV_F32 = 0, RKV_BF16 = 1 } rkv_dtype;
+
+typedef struct rkv_attn_dims {
+  int32_t q_len;        /* queries in the verify block, >= 1 (16 for a 16-token draft) */
+  int32_t n_q_heads;    /* Hq, a multiple of n_kv_heads */
+  int32_t n_kv_heads;   /* Hkv >= 1 */
+  int32_t head_dim;     /* 64 or 128 */
+  float scale;          /* softmax scale; 0 selects 1/sqrt(head_dim) */
+  int32_t dtype;        /* rkv_dtype of Q, K and V */
+} rkv_attn_dims;
+
+int32_t rkv_abi_version(void);
+const char* rkv_status_str(int32_t status);
+
+/* ---------------------------------------------------------------------------------
+ * Contiguous reference layout (GPU-side reference for the chunked calls, and plain
+ * decode with q_len = 1).  Keys are positions 0 .. ctx_len-1 in k, v
+ * [ctx_len][Hkv][D]; query i sits at ctx_len - q_len + i.  window = 0: full causal,
+ * window > 0: sliding window of that many keys.  dtype f32 or bf16; every
+ * arithmetic step runs in f32.  num_splits = 0 picks a split of the key range;
+ * any value gives the same result up to f32 rounding.
+ * ------------------------------------------------------------------------------- */
+size_t decode_attn_ref_layout_workspace_bytes(const rkv_attn_dims* dims, int64_t ctx_len,
+                                              int32_t num_splits);
+int32_t decode_attn_ref_layout(const rkv_attn_dims* dims, const void* q, const void* k,
+                               const void* v, int64_t ctx_len, int32_t window,
+                               int32_t num_splits, void* workspace, size_t workspace_bytes,
+                               float* out, float* lse, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Sliding-window verify attention over a position ring (lucebox post, "3. Ring caches
+ * for the sliding-window layers": window layers keep a ring, slot = pos mod 2048, and
+ * skip the pager).
+ *   pos0       absolute position of query 0; query i sits at pos0 + i
+ *   ring_head  the slot of query 0; must equal pos0 mod ring_size (checked)
+ *   ring_size  positions the ring holds, a multiple of 64, >= window + q_len - 1
+ *   window     keys per query including its own position, >= 1
+ * The ring must hold positions max(0, pos0+q_len-ring_size) .. pos0+q_len-1, the
+ * block's own rows included.  k_ring [ring_size/64][Hkv][64][D], v_ring
+ * [ring_size/64][Hkv][D][64], bf16; Q bf16.  Slots holding no position may contain
+ * anything (they are masked and never multiply a result).
+ * ------------------------------------------------------------------------------- */
+size_t verify_attn_ring_workspace_bytes(const rkv_attn_dims* dims, int32_t ring_size,
+                                        int32_t window, int32_t num_splits);
+int32_t verify_attn_ring(const rkv_attn_dims* dims, const void* q, const void* k_ring,
+                         const void* v_ring, int64_t pos0, int32_t ring_head,
+                         int32_t ring_size, int32_t window, int32_t num_splits,
+                         void* workspace, size_t workspace_bytes, float* out, float* lse,
+                         void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Full-attention verify attention over the paged pool of 64-token chunks (lucebox
+ * post, "Three optimizations", item 1).  Keys are positions 0 .. ctx_len-1; query i
+ * sits at ctx_len - q_len + i (ctx_len counts the block).  Logical chunk c lives in
+ * pool slot page_table[c] (device int32 array of n_table >= ceil(ctx_len/64)
+ * entries); k_pool [n_slots][Hkv][64][D], v_pool [n_slots][Hkv][D][64], bf16; Q
+ * bf16.  chunk_size must be 64.  Positions >= ctx_len in the last chunk may hold
+ * anything.  An entry outside [0, n_slots) is never dereferenced: its chunk
+ * contributes nothing (a contract breach, not an error the call can report).
+ *
+ * The key range is split into num_splits ranges of whole chunks (0: chosen from the
+ * context and the chip's 256 compute units); each range yields a partial result
+ * and a log-sum-exp merge combines them.  Any split gives the same result up to
+ * f32 rounding.
+ * ------------------------------------------------------------------------------- */
+size_t verify_attn_paged_workspace_bytes(const rkv_attn_dims* dims, int64_t ctx_len,
+                                         int32_t chunk_size, int32_t num_splits);
+int32_t verify_attn_paged(const rkv_attn_dims* dims, const void* q, const void* k_pool,
+                          const void* v_pool, const int32_t* page_table, int32_t n_table,
+                          int32_t n_slots, int32_t chunk_size, int64_t ctx_len,
+                          int32_t num_splits, void* workspace, size_t workspace_bytes,
+                          float* out, float* lse, void* stream);
+
+/* Split count verify_attn_paged uses for num_splits = 0 (host-only, no HIP call). */
+int32_t verify_attn_paged_auto_splits(const rkv_attn_dims* dims, int64_t ctx_len,
+                                      int32_t chunk_size);
+
+/* ---------------------------------------------------------------------------------
+ * The paged call in two phases, for callers that time or distribute them (partials
+ * of disjoint key ranges, e.g. computed on different devices, merge the same way).
+ * Split s covers logical chunks [s*cps, min((s+1)*cps, n_chunks)) with n_chunks =
+ * ceil(ctx_len/64), cps = ceil(n_chunks/num_splits); num_splits >= 1 here.
+ *   part_out  [n_kv_heads][num_splits][q_len*G][D] f32: the split's normalised output
+ *   part_lse  [n_kv_heads][num_splits][q_len*G]    f32: natural-log lse over the split's
+ *             keys, -inf where a row sees no key of the split (then part_out row = 0)
+ * Row r of a KV head is query r / G, query head g*G + r % G.
+ * ------------------------------------------------------------------------------- */
+int32_t verify_attn_paged_partial(const rkv_attn_dims* dims, const void* q,
+                                  const void* k_pool, const void* v_pool,
+                                  const int32_t* page_table, int32_t n_table, int32_t n_slots,
+                                  int32_t chunk_size, int64_t ctx_len, int32_t num_splits,
+                                  float* part_out, float* part_lse, void* stream);
+
+/* Log-sum-exp merge of num_splits partials laid out as above:
+ *   M = max_s lse_s, w_s = exp(lse_s - M), out = sum_s w_s O_s / sum_s w_s,
+ *   lse = M + ln sum_s w_s   (splits with lse_s = -inf carry no weight).
+ * dims->dtype is ignored.  out [q_len][Hq][D] f32, lse [q_len][Hq] f32 or NULL. */
+int32_t attn_merge_partials(const rkv_attn_dims* dims, int32_t num_splits,
+                            const float* part_out, const float* part_lse, float* out,
+                            float* lse, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Greedy acceptance (lucebox post, "TL;DR" and "The model, fast MoE with a drafter in
+ * the box": verify-exact speculative decoding, exact greedy equivalence).
+ *   logits     [n_draft+1][vocab] f32, finite; row r is the target's distribution
+ *              after the committed prefix and drafts 0..r-1
+ *   proposals  [n_draft] int32 drafted tokens
+ * t_r = the first index of the maximum of row r (float32 compare, -0 == +0);
+ * a = the first r < n_draft with t_r != proposals[r], else n_draft.
+ *   accept_len [1] int32 <- a
+ *   committed  [n_draft+1] int32 <- proposals[0..a) then t_a; entries after a are -1
+ *   row_argmax [n_draft+1] int32 <- t_r (may be NULL)
+ * 0 <= n_draft <= 255, vocab >= 1.  NaN logits give an unspecified (but in-range)
+ * result.
+ * ------------------------------------------------------------------------------- */
+size_t verify_accept_workspace_bytes(int32_t n_draft, int32_t vocab);
+int32_t verify_accept(const float* logits, int32_t n_draft, int32_t vocab,
+                      const int32_t* proposals, int32_t* accept_len, int32_t* committed,
+                      int32_t* row_argmax, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Layout helpers: copy n contiguous rows k_src, v_src [n][Hkv][D] holding positions
+ * pos_first .. pos_first+n-1 into a ring (slot = pos mod ring_size) or into the
+ * paged pool (slot page_table[pos/64], offset pos mod 64), K key-major and V
+ * dimension-major per chunk.  This is also how a verify block's own rows are
+ * appended before attention.  dtype must be bf16.  For the ring, n <= ring_size.
+ * Pool entries outside [0, n_slots) are skipped on the device.
+ * ------------------------------------------------------------------------------- */
+int32_t ref_layout_to_ring(const void* k_src, const void* v_src, int64_t pos_first, int64_t n,
+                           int32_t n_kv_heads, int32_t head_dim, int32_t dtype, void* k_ring,
+                           void* v_ring, int32_t ring_size, void* stream);
+int32_t ref_layout_to_paged(const void* k_src, const void* v_src, int64_t pos_first,
+                            int64_t n, int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
+                            void* k_pool, void* v_pool, const int32_t* page_table,
+                            int32_t n_table, int32_t n_slots, int32_t chunk_size,
+                            void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RING_KV_H */

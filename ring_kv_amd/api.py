@@ -1,0 +1,250 @@
+"""Torch-tensor front end of libring_kv.  Argument marshalling only: every step of the verify
+path runs in the library's HIP kernels; torch supplies device memory and the stream.
+
+Layouts are those of include/ring_kv.h: Q [q_len][Hq][D]; chunked K [slots][Hkv][64][D] and
+V [slots][Hkv][D][64] (bf16); out [q_len][Hq][D] and lse [q_len][Hq] float32.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from ._lib import RKV_BF16, RKV_F32, AttnDims, check, lib
+
+CHUNK = 64
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, ndim=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dims(q: torch.Tensor, n_kv_heads: int, scale: float) -> AttnDims:
+    q_len, hq, d = q.shape
+    dt = RKV_BF16 if q.dtype == torch.bfloat16 else RKV_F32
+    return AttnDims(q_len, hq, n_kv_heads, d, float(scale), dt)
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return None, 0
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, need {nbytes}")
+        return ws, ws.numel() * ws.element_size()
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def _outputs(q, out, lse, want_lse):
+    q_len, hq, d = q.shape
+    if out is None:
+        out = torch.empty((q_len, hq, d), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((q_len, hq), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, 3, q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2, q.device)
+    return out, lse
+
+
+def verify_attn_paged(q, k_pool, v_pool, page_table, ctx_len: int, *, num_splits: int = 0,
+                      scale: float = 0.0, out=None, lse=None, want_lse: bool = True,
+                      workspace=None, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Full-attention verify block over the paged pool of 64-token chunks."""
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _need(k_pool, "k_pool", torch.bfloat16, 4, dev)
+    _need(v_pool, "v_pool", torch.bfloat16, 4, dev)
+    _need(page_table, "page_table", torch.int32, 1, dev)
+    n_slots, hkv, chunk, d = k_pool.shape
+    if tuple(v_pool.shape) != (n_slots, hkv, d, chunk):
+        raise ValueError("v_pool must be [slots][Hkv][D][64]")
+    dims = _dims(q, hkv, scale)
+    L = lib()
+    ws, wsb = _workspace(L.verify_attn_paged_workspace_bytes(ctypes.byref(dims), ctx_len, chunk,
+                                                             num_splits), dev, workspace)
+    out, lse = _outputs(q, out, lse, want_lse)
+    check("verify_attn_paged", L.verify_attn_paged(
+        ctypes.byref(dims), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
+        page_table.numel(), n_slots, chunk, ctx_len, num_splits, _ptr(ws), wsb, _ptr(out),
+        _ptr(lse), _stream(stream, dev)))
+    return out, lse
+
+
+def verify_attn_paged_auto_splits(n_q_heads: int, n_kv_heads: int, head_dim: int, q_len: int,
+                                  ctx_len: int) -> int:
+    dims = AttnDims(q_len, n_q_heads, n_kv_heads, head_dim, 0.0, RKV_BF16)
+    return lib().verify_attn_paged_auto_splits(ctypes.byref(dims), ctx_len, CHUNK)
+
+
+def verify_attn_paged_partial(q, k_pool, v_pool, page_table, ctx_len: int, num_splits: int, *,
+                              scale: float = 0.0, part_out=None, part_lse=None, stream=None):
+    """Phase one of the paged call: per split of the chunk range, the normalised output
+    [Hkv][S][rows][D] and the split's lse [Hkv][S][rows]."""
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    n_slots, hkv, chunk, d = k_pool.shape
+    q_len, hq, _ = q.shape
+    rows = q_len * (hq // hkv)
+    if part_out is None:
+        part_out = torch.empty((hkv, num_splits, rows, d), dtype=torch.float32, device=dev)
+    if part_lse is None:
+        part_lse = torch.empty((hkv, num_splits, rows), dtype=torch.float32, device=dev)
+    for t, n in ((k_pool, "k_pool"), (v_pool, "v_pool")):
+        _need(t, n, torch.bfloat16, 4, dev)
+    _need(page_table, "page_table", torch.int32, 1, dev)
+    _need(part_out, "part_out", torch.float32, 4, dev)
+    _need(part_lse, "part_lse", torch.float32, 3, dev)
+    dims = _dims(q, hkv, scale)
+    check("verify_attn_paged_partial", lib().verify_attn_paged_partial(
+        ctypes.byref(dims), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
+        page_table.numel(), n_slots, chunk, ctx_len, num_splits, _ptr(part_out), _ptr(part_lse),
+        _stream(stream, dev)))
+    return part_out, part_lse
+
+
+def attn_merge_partials(part_out, part_lse, q_len: int, n_q_heads: int, *, out=None, lse=None,
+                        want_lse: bool = True, stream=None):
+    """Log-sum-exp merge of split partials (layout of verify_attn_paged_partial)."""
+    _need(part_out, "part_out", torch.float32, 4)
+    dev = part_out.device
+    _need(part_lse, "part_lse", torch.float32, 3, dev)
+    hkv, S, rows, d = part_out.shape
+    dims = AttnDims(q_len, n_q_heads, hkv, d, 0.0, RKV_BF16)
+    if out is None:
+        out = torch.empty((q_len, n_q_heads, d), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((q_len, n_q_heads), dtype=torch.float32, device=dev)
+    check("attn_merge_partials", lib().attn_merge_partials(
+        ctypes.byref(dims), S, _ptr(part_out), _ptr(part_lse), _ptr(out), _ptr(lse),
+        _stream(stream, dev)))
+    return out, lse
+
+
+def verify_attn_ring(q, k_ring, v_ring, pos0: int, window: int, *, num_splits: int = 0,
+                     scale: float = 0.0, out=None, lse=None, want_lse: bool = True,
+                     workspace=None, stream=None):
+    """Sliding-window verify block over the position ring (slot = pos mod ring_size)."""
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _need(k_ring, "k_ring", torch.bfloat16, 4, dev)
+    _need(v_ring, "v_ring", torch.bfloat16, 4, dev)
+    n_chunks, hkv, chunk, d = k_ring.shape
+    if tuple(v_ring.shape) != (n_chunks, hkv, d, chunk):
+        raise ValueError("v_ring must be [ring/64][Hkv][D][64]")
+    ring_size = n_chunks * chunk
+    dims = _dims(q, hkv, scale)
+    L = lib()
+    ws, wsb = _workspace(L.verify_attn_ring_workspace_bytes(ctypes.byref(dims), ring_size, window,
+                                                            num_splits), dev, workspace)
+    out, lse = _outputs(q, out, lse, want_lse)
+    check("verify_attn_ring", L.verify_attn_ring(
+        ctypes.byref(dims), _ptr(q), _ptr(k_ring), _ptr(v_ring), pos0, pos0 % ring_size,
+        ring_size, window, num_splits, _ptr(ws), wsb, _ptr(out), _ptr(lse), _stream(stream, dev)))
+    return out, lse
+
+
+def decode_attn_ref_layout(q, k, v, ctx_len: int, window: int = 0, *, num_splits: int = 0,
+                           scale: float = 0.0, out=None, lse=None, want_lse: bool = True,
+                           workspace=None, stream=None):
+    """Verify/decode attention over the contiguous layout K, V [ctx][Hkv][D] (f32 or bf16)."""
+    _need(q, "q", (torch.float32, torch.bfloat16), 3)
+    dev = q.device
+    _need(k, "k", q.dtype, 3, dev)
+    _need(v, "v", q.dtype, 3, dev)
+    hkv = k.shape[1]
+    if k.shape[0] < ctx_len or v.shape[0] < ctx_len:
+        raise ValueError("k, v hold fewer than ctx_len rows")
+    dims = _dims(q, hkv, scale)
+    L = lib()
+    ws, wsb = _workspace(L.decode_attn_ref_layout_workspace_bytes(ctypes.byref(dims), ctx_len,
+                                                                  num_splits), dev, workspace)
+    out, lse = _outputs(q, out, lse, want_lse)
+    check("decode_attn_ref_layout", L.decode_attn_ref_layout(
+        ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), ctx_len, window, num_splits, _ptr(ws), wsb,
+        _ptr(out), _ptr(lse), _stream(stream, dev)))
+    return out, lse
+
+
+def verify_accept(logits, proposals, *, accept_len=None, committed=None, row_argmax=None,
+                  want_argmax: bool = True, workspace=None, stream=None):
+    """Greedy acceptance: (accept_len [1], committed [k+1] (-1 after a+1), row_argmax [k+1])."""
+    _need(logits, "logits", torch.float32, 2)
+    dev = logits.device
+    _need(proposals, "proposals", torch.int32, 1, dev)
+    k = proposals.numel()
+    if logits.shape[0] != k + 1:
+        raise ValueError("need k+1 logit rows for k proposals")
+    vocab = logits.shape[1]
+    if accept_len is None:
+        accept_len = torch.empty(1, dtype=torch.int32, device=dev)
+    if committed is None:
+        committed = torch.empty(k + 1, dtype=torch.int32, device=dev)
+    if row_argmax is None and want_argmax:
+        row_argmax = torch.empty(k + 1, dtype=torch.int32, device=dev)
+    L = lib()
+    ws, wsb = _workspace(L.verify_accept_workspace_bytes(k, vocab), dev, workspace)
+    check("verify_accept", L.verify_accept(
+        _ptr(logits), k, vocab, _ptr(proposals), _ptr(accept_len), _ptr(committed),
+        _ptr(row_argmax), _ptr(ws), wsb, _stream(stream, dev)))
+    return accept_len, committed, row_argmax
+
+
+def ref_layout_to_ring(k_src, v_src, pos_first: int, k_ring, v_ring, *, stream=None):
+    """Write rows k_src, v_src [n][Hkv][D] (positions pos_first..) into the ring."""
+    _need(k_src, "k_src", torch.bfloat16, 3)
+    dev = k_src.device
+    for t, n in ((v_src, "v_src"), (k_ring, "k_ring"), (v_ring, "v_ring")):
+        _need(t, n, torch.bfloat16, None, dev)
+    n, hkv, d = k_src.shape
+    ring_size = k_ring.shape[0] * CHUNK
+    check("ref_layout_to_ring", lib().ref_layout_to_ring(
+        _ptr(k_src), _ptr(v_src), pos_first, n, hkv, d, RKV_BF16, _ptr(k_ring), _ptr(v_ring),
+        ring_size, _stream(stream, dev)))
+
+
+def ref_layout_to_paged(k_src, v_src, pos_first: int, k_pool, v_pool, page_table, *,
+                        stream=None):
+    """Write rows k_src, v_src [n][Hkv][D] (positions pos_first..) into the paged pool."""
+    _need(k_src, "k_src", torch.bfloat16, 3)
+    dev = k_src.device
+    for t, n in ((v_src, "v_src"), (k_pool, "k_pool"), (v_pool, "v_pool")):
+        _need(t, n, torch.bfloat16, None, dev)
+    _need(page_table, "page_table", torch.int32, 1, dev)
+    n, hkv, d = k_src.shape
+    check("ref_layout_to_paged", lib().ref_layout_to_paged(
+        _ptr(k_src), _ptr(v_src), pos_first, n, hkv, d, RKV_BF16, _ptr(k_pool), _ptr(v_pool),
+        _ptr(page_table), page_table.numel(), k_pool.shape[0], CHUNK, _stream(stream, dev)))
+
+
+def tensor_from_numpy(arr, device="cuda", bf16_bits: Optional[bool] = None) -> torch.Tensor:
+    """Copy a numpy array to the device; uint16 arrays are bf16 bit patterns."""
+    import numpy as np
+    a = np.ascontiguousarray(arr)
+    if bf16_bits is None:
+        bf16_bits = a.dtype == np.uint16
+    if bf16_bits:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a).to(device)

@@ -1,0 +1,92 @@
+// Internal launch interface between the C entry points (abi.hip) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rkv {
+
+// Attention of one verify block over a chunked KV store (paged pool or position ring),
+// split over ranges of whole chunks.  Rows of a KV head: r = i * G + (h - g * G).
+struct ChunkAttnArgs {
+  const uint16_t* q;      // [q_len][Hq][D] bf16
+  const uint16_t* k;      // [n_slots][Hkv][64][D] bf16
+  const uint16_t* v;      // [n_slots][Hkv][D][64] bf16
+  const int32_t* pt;      // page table; nullptr selects the ring (slot = c mod n_slots)
+  int32_t n_slots;        // pool slots, or ring chunk slots
+  int32_t q_len, G, n_q_heads, n_kv_heads, head_dim;
+  int64_t p0;             // position of query 0
+  int32_t window;         // 0: full causal
+  int64_t valid_lo;       // the store holds positions [valid_lo, valid_hi)
+  int64_t valid_hi;
+  int64_t c_first;        // first logical chunk of split 0
+  int64_t n_chunks;       // logical chunks covered by all splits
+  int32_t cps;            // chunks per split
+  int32_t num_splits;
+  float scale_log2;       // softmax scale * log2(e)
+  float* out;             // part_o == nullptr: final output [q_len][Hq][D]
+  float* lse;             //                    and lse [q_len][Hq] (may be nullptr)
+  float* part_o;          // otherwise partials [Hkv][S][rows][D]
+  float* part_lse;        //                    and [Hkv][S][rows]
+};
+hipError_t launch_chunk_attn(const ChunkAttnArgs& a, hipStream_t stream);
+
+struct MergeArgs {
+  const float* part_o;
+  const float* part_lse;
+  float* out;
+  float* lse;
+  int32_t q_len, G, n_q_heads, n_kv_heads, head_dim, num_splits;
+};
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+
+// Contiguous-layout attention (f32 arithmetic), same partial format as above.
+struct ContigArgs {
+  const void* q;          // [q_len][Hq][D]
+  const void* k;          // [ctx][Hkv][D]
+  const void* v;
+  int32_t dtype;          // 0 f32, 1 bf16
+  int32_t q_len, G, n_q_heads, n_kv_heads, head_dim;
+  int64_t ctx_len;
+  int32_t window;
+  int64_t c_first;        // first 64-key tile of split 0 (tiles below every window are skipped)
+  int64_t n_chunks;       // tiles covered by all splits
+  int32_t cps;
+  int32_t num_splits;
+  float scale_log2;
+  float* out;
+  float* lse;
+  float* part_o;
+  float* part_lse;
+};
+hipError_t launch_contig_attn(const ContigArgs& a, hipStream_t stream);
+
+struct AcceptArgs {
+  const float* logits;
+  int32_t n_rows;         // n_draft + 1
+  int32_t vocab;
+  const int32_t* proposals;
+  int32_t* accept_len;
+  int32_t* committed;
+  int32_t* row_argmax;    // may be nullptr
+  float* part_val;        // [n_rows][parts]
+  int32_t* part_idx;      // [n_rows][parts]
+  int32_t parts;
+  int32_t part_len;
+};
+hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream);
+
+struct ScatterArgs {
+  const uint16_t* k_src;  // [n][Hkv][D]
+  const uint16_t* v_src;
+  int64_t pos_first, n;
+  int32_t n_kv_heads, head_dim;
+  uint16_t* k_dst;        // chunked store
+  uint16_t* v_dst;
+  const int32_t* pt;      // nullptr: ring
+  int32_t n_table;        // page table entries (paged)
+  int32_t n_slots;        // pool slots, or ring chunk slots
+  int64_t ring_size;
+};
+hipError_t launch_scatter(const ScatterArgs& a, hipStream_t stream);
+
+}  // namespace rkv

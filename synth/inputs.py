@@ -2,10 +2,15 @@
 planted logits.
 
 Seed scheme: every tensor of every workload comes from its own numpy
-``Generator`` seeded with ``SeedSequence([2026, workload_id, layer, stream])``,
-so the same call always yields the same bytes on any machine.
+``Generator`` seeded with ``SeedSequence([2026, workload_id, layer, stream])``;
+K/V rows are drawn in blocks of 8192 rows, block b seeded with
+``SeedSequence([2026, workload_id, layer, stream, b])``.  The same call always
+yields the same bytes on any machine.
 """
 from __future__ import annotations
+
+import concurrent.futures as cf
+import os
 
 import numpy as np
 
@@ -14,7 +19,7 @@ __all__ = [
     "STREAM_LOGITS", "STREAM_PREFIX", "STREAM_TARGET", "CHUNK",
     "stream", "round_f32_to_bf16_bits", "bf16_bits_to_f32", "normal_bits",
     "normal_f32", "scatter_chunked", "paged_store", "ring_store", "ring_positions",
-    "planted_logits", "planted_proposals", "NAN_BF16",
+    "planted_logits", "planted_proposals", "NAN_BF16", "blocked_rows", "ROW_BLOCK",
 ]
 
 ROOT_SEED = 2026
@@ -58,6 +63,44 @@ def normal_bits(g: np.random.Generator, shape) -> np.ndarray:
     return round_f32_to_bf16_bits(normal_f32(g, shape))
 
 
+#: rows per independently seeded block of a large K/V draw
+ROW_BLOCK = 8192
+
+
+def _pool_size() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def blocked_rows(workload_id: int, layer: int, stream_id: int, n: int, row_shape, fn):
+    """``[n, *row_shape]`` built block by block: block b (rows b*ROW_BLOCK ..) is
+    ``fn(generator, rows)`` with its own generator seeded by
+    ``SeedSequence([2026, workload_id, layer, stream_id, b])``.  Blocks are filled in a
+    thread pool; the result does not depend on the number of threads."""
+    nb = -(-n // ROW_BLOCK)
+    first = None
+    out = None
+
+    def one(b):
+        rows = min(ROW_BLOCK, n - b * ROW_BLOCK)
+        g = np.random.default_rng(np.random.SeedSequence(
+            [ROOT_SEED, int(workload_id), int(layer), int(stream_id), int(b)]))
+        return b, fn(g, (rows, *row_shape))
+
+    if nb == 0:
+        return None
+    with cf.ThreadPoolExecutor(_pool_size()) as ex:
+        for b, arr in ex.map(one, range(nb)):
+            if out is None:
+                first = arr
+                out = np.empty((n, *row_shape), dtype=first.dtype)
+            out[b * ROW_BLOCK:b * ROW_BLOCK + len(arr)] = arr
+    return out
+
+
 def scatter_chunked(k_rows, v_rows, first_pos: int, slot_of_chunk, n_slots: int,
                     chunk: int = CHUNK, fill=None):
     """Scatter contiguous rows into the chunked store layout.
@@ -74,27 +117,36 @@ def scatter_chunked(k_rows, v_rows, first_pos: int, slot_of_chunk, n_slots: int,
     dt = k_rows.dtype
     if fill is None:
         fill = NAN_BF16 if dt == np.uint16 else np.float32(np.nan)
-    K = np.full((n_slots, hkv, chunk, d), fill, dtype=dt)
-    V = np.full((n_slots, hkv, d, chunk), fill, dtype=dt)
+    K = np.empty((n_slots, hkv, chunk, d), dtype=dt)
+    V = np.empty((n_slots, hkv, d, chunk), dtype=dt)
     if n == 0:
+        K[...] = fill
+        V[...] = fill
         return K, V
     c_first = first_pos // chunk
     c_last = (first_pos + n - 1) // chunk
-    lead = first_pos - c_first * chunk
-    span = (c_last - c_first + 1) * chunk
-    # pad to whole chunks with the fill value, then move whole chunks at once
-    kp = np.full((span, hkv, d), fill, dtype=dt)
-    vp = np.full((span, hkv, d), fill, dtype=dt)
-    kp[lead:lead + n] = k_rows
-    vp[lead:lead + n] = v_rows
-    kc = kp.reshape(-1, chunk, hkv, d).transpose(0, 2, 1, 3)   # [c][Hkv][chunk][D]
-    vc = vp.reshape(-1, chunk, hkv, d).transpose(0, 2, 3, 1)   # [c][Hkv][D][chunk]
     slots = np.array([slot_of_chunk(c) for c in range(c_first, c_last + 1)], dtype=np.int64)
     if len(np.unique(slots)) != len(slots):
         raise ValueError("two chunks of the span map to the same slot")
-    # a partially covered chunk keeps the fill value in its uncovered part
-    K[slots] = kc
-    V[slots] = vc
+    covered = np.zeros(n_slots, dtype=bool)
+    covered[slots] = True
+    K[~covered] = fill
+    V[~covered] = fill
+    for idx, c in enumerate(range(c_first, c_last + 1)):
+        lo = max(first_pos, c * chunk)
+        hi = min(first_pos + n, (c + 1) * chunk)
+        rk = k_rows[lo - first_pos:hi - first_pos]
+        rv = v_rows[lo - first_pos:hi - first_pos]
+        sl = slots[idx]
+        if hi - lo == chunk:
+            K[sl] = rk.transpose(1, 0, 2)          # [Hkv][chunk][D]
+            V[sl] = rv.transpose(1, 2, 0)          # [Hkv][D][chunk]
+        else:
+            # a partially covered chunk keeps the fill value in its uncovered part
+            K[sl] = fill
+            V[sl] = fill
+            K[sl, :, lo - c * chunk:hi - c * chunk, :] = rk.transpose(1, 0, 2)
+            V[sl, :, :, lo - c * chunk:hi - c * chunk] = rv.transpose(1, 2, 0)
     return K, V
 
 

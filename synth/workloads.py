@@ -20,7 +20,7 @@ from typing import Optional
 
 import numpy as np
 
-from .inputs import (CHUNK, STREAM_K, STREAM_LOGITS, STREAM_OUTLIER, STREAM_PERM,
+from .inputs import (CHUNK, STREAM_K, blocked_rows, STREAM_LOGITS, STREAM_OUTLIER, STREAM_PERM,
                      STREAM_PREFIX, STREAM_Q, STREAM_V, normal_bits, normal_f32,
                      paged_store, planted_logits, planted_proposals,
                      round_f32_to_bf16_bits, ring_positions, ring_store, stream)
@@ -96,14 +96,21 @@ def _draw(wid, layer, sid, shape, dtype):
 
 
 def _kv_rows(wid, layer, n, hkv, d, dtype, outlier_rate=0.0, outlier_shift=4.0):
+    """K and V rows [n][Hkv][D] ~ N(0,1); with ``outlier_rate`` > 0 each (row, KV head) of K
+    is shifted by +outlier_shift on every element with that probability (before rounding)."""
     if dtype == "f32":
-        return _draw(wid, layer, STREAM_K, (n, hkv, d), "f32"), _draw(wid, layer, STREAM_V, (n, hkv, d), "f32")
-    k = normal_f32(stream(wid, layer, STREAM_K), (n, hkv, d))
-    if outlier_rate > 0:
-        sel = stream(wid, layer, STREAM_OUTLIER).random((n, hkv)) < outlier_rate
-        k[sel] += np.float32(outlier_shift)
-    k = round_f32_to_bf16_bits(k)
-    v = normal_bits(stream(wid, layer, STREAM_V), (n, hkv, d))
+        return (blocked_rows(wid, layer, STREAM_K, n, (hkv, d), normal_f32),
+                blocked_rows(wid, layer, STREAM_V, n, (hkv, d), normal_f32))
+
+    def k_block(g, shape):
+        x = normal_f32(g, shape)
+        if outlier_rate > 0:
+            sel = g.random(shape[:2]) < outlier_rate
+            x[sel] += np.float32(outlier_shift)
+        return round_f32_to_bf16_bits(x)
+
+    k = blocked_rows(wid, layer, STREAM_K, n, (hkv, d), k_block)
+    v = blocked_rows(wid, layer, STREAM_V, n, (hkv, d), normal_bits)
     return k, v
 
 

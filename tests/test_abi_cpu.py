@@ -1,0 +1,117 @@
+"""The C library loads without a GPU, exports every function include/ring_kv.h declares, and
+rejects bad arguments on the host with the documented status before any HIP call (a call that
+reached a launch here, with no GPU, would report RKV_ERR_HIP instead)."""
+import ctypes
+import os
+
+import pytest
+
+from ring_kv_amd import _lib
+from ring_kv_amd._lib import AttnDims
+
+if not os.path.exists(_lib.LIB_PATH):
+    pytest.skip("libring_kv.so not built (run python -m ring_kv_amd.build)", allow_module_level=True)
+
+L = _lib.lib()
+NULL = None
+P = ctypes.c_void_p(0x1000)          # never dereferenced: every call below stops on the host
+OK, ENULL, ESHAPE, EDTYPE, ERING, ETABLE, EWS, EHIP, EARG = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+
+def dims(q_len=16, hq=16, hkv=4, d=128, scale=0.0, dtype=1):
+    return ctypes.byref(AttnDims(q_len, hq, hkv, d, scale, dtype))
+
+
+def test_exports_every_declared_function():
+    names = _lib.declared_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.rkv_abi_version() == 1
+    assert L.rkv_status_str(-6) == b"workspace missing or too small"
+
+
+def paged(d=None, q=P, k=P, v=P, pt=P, n_table=4096, n_slots=4096, chunk=64, ctx=262144,
+          splits=0, ws=P, wsb=1 << 30, out=P):
+    return L.verify_attn_paged(dims() if d is None else d, q, k, v, pt, n_table, n_slots, chunk,
+                               ctx, splits, ws, wsb, out, NULL, NULL)
+
+
+def test_paged_argument_checks():
+    assert L.verify_attn_paged(None, P, P, P, P, 4096, 4096, 64, 262144, 0, P, 1 << 30, P, NULL, NULL) == ENULL
+    assert paged(q=NULL) == ENULL and paged(pt=NULL) == ENULL and paged(out=NULL) == ENULL
+    assert paged(d=dims(d=96)) == ESHAPE
+    assert paged(d=dims(hq=10, hkv=4)) == ESHAPE
+    assert paged(d=dims(q_len=65)) == ESHAPE            # 65 * 4 rows > 256
+    assert paged(d=dims(q_len=0)) == ESHAPE
+    assert paged(d=dims(dtype=0)) == EDTYPE               # the chunked stores are bf16
+    assert paged(d=dims(dtype=7)) == EDTYPE
+    assert paged(d=dims(scale=-1.0)) == EARG
+    assert paged(chunk=32) == ETABLE
+    assert paged(n_table=4095) == ETABLE
+    assert paged(n_slots=0) == ETABLE
+    assert paged(ctx=15) == ESHAPE                        # the block must fit in the context
+    assert paged(ws=NULL) == EWS
+    assert paged(wsb=1000) == EWS
+    assert paged(splits=-1) == EARG
+
+
+def test_paged_workspace_and_splits():
+    d = dims()
+    # 4 KV heads: 64 splits of 64 chunks at 262,144 positions; partials [4][64][64][128] f32
+    assert L.verify_attn_paged_auto_splits(d, 262144, 64) == 64
+    want = 4 * 64 * 64 * 128 * 4 + 4 * 64 * 64 * 4
+    assert L.verify_attn_paged_workspace_bytes(d, 262144, 64, 0) == want
+    assert L.verify_attn_paged_workspace_bytes(d, 262144, 64, 1) == 0     # no merge, no partials
+    assert L.verify_attn_paged_auto_splits(d, 8192, 64) == 64            # 2 chunks per split
+    assert L.verify_attn_paged_auto_splits(d, 131072, 64) == 64
+    assert L.verify_attn_paged_auto_splits(d, 65, 64) == 2
+    assert L.verify_attn_paged_workspace_bytes(d, 262144, 32, 0) == 0    # unsupported chunk
+
+
+def ring(d=None, pos0=30000, head=1328, size=2048, window=512, splits=0, ws=P, wsb=1 << 30):
+    return L.verify_attn_ring(dims() if d is None else d, P, P, P, pos0, head, size, window,
+                              splits, ws, wsb, P, NULL, NULL)
+
+
+def test_ring_argument_checks():
+    assert ring(head=1327) == ERING                        # head must be pos0 mod ring_size
+    assert ring(size=2000, head=30000 % 2000) == ERING     # not a multiple of 64
+    assert ring(size=512, head=30000 % 512) == ERING       # 512 < window + q_len - 1
+    assert ring(window=0) == EARG
+    assert ring(pos0=-1, head=0) == EARG
+    assert ring(d=dims(dtype=0)) == EDTYPE
+    assert ring(ws=NULL) == EWS
+    # 527 positions touch at most 10 chunks: 10 splits of one chunk by default
+    want = 4 * 10 * 64 * 128 * 4 + 4 * 10 * 64 * 4
+    assert L.verify_attn_ring_workspace_bytes(dims(), 2048, 512, 0) == want
+
+
+def test_contiguous_and_merge_checks():
+    d = dims(q_len=16, hq=8, hkv=2, d=64, dtype=0)
+    assert L.decode_attn_ref_layout(d, P, P, P, 1024, 0, 0, NULL, 0, P, NULL, NULL) == EWS
+    assert L.decode_attn_ref_layout(d, P, P, P, 8, 0, 0, P, 1 << 20, P, NULL, NULL) == ESHAPE
+    assert L.decode_attn_ref_layout(d, P, P, P, 1024, -1, 0, P, 1 << 20, P, NULL, NULL) == EARG
+    assert L.decode_attn_ref_layout(d, NULL, P, P, 1024, 0, 0, P, 1 << 20, P, NULL, NULL) == ENULL
+    assert L.attn_merge_partials(dims(), 0, P, P, P, NULL, NULL) == EARG
+    assert L.attn_merge_partials(dims(), 4, NULL, P, P, NULL, NULL) == ENULL
+    assert L.verify_attn_paged_partial(dims(), P, P, P, P, 128, 128, 64, 8192, 0, P, P, NULL) == EARG
+
+
+def test_accept_checks():
+    need = L.verify_accept_workspace_bytes(16, 65536)
+    assert need == 2 * 1280           # 17 rows x 16 parts of 4096 logits, f32 + i32, 256-B aligned
+    assert L.verify_accept(NULL, 16, 65536, P, P, P, NULL, P, need, NULL) == ENULL
+    assert L.verify_accept(P, 16, 65536, P, P, P, NULL, NULL, 0, NULL) == EWS
+    assert L.verify_accept(P, 16, 65536, P, P, P, NULL, P, need - 1, NULL) == EWS
+    assert L.verify_accept(P, 256, 10, P, P, P, NULL, P, 1 << 20, NULL) == ESHAPE
+    assert L.verify_accept(P, 16, 0, P, P, P, NULL, P, 1 << 20, NULL) == ESHAPE
+    assert L.verify_accept(P, 3, 10, NULL, P, P, NULL, P, 1 << 20, NULL) == ENULL
+
+
+def test_layout_helper_checks():
+    assert L.ref_layout_to_ring(P, P, 0, 3000, 4, 128, 1, P, P, 2048, NULL) == ERING
+    assert L.ref_layout_to_ring(P, P, 0, 10, 4, 128, 0, P, P, 2048, NULL) == EDTYPE
+    assert L.ref_layout_to_paged(P, P, 0, 8193, 4, 128, 1, P, P, P, 128, 128, 64, NULL) == ETABLE
+    assert L.ref_layout_to_paged(P, P, 0, 10, 4, 96, 1, P, P, P, 128, 128, 64, NULL) == ESHAPE
+    assert L.ref_layout_to_paged(NULL, P, 0, 0, 4, 128, 1, P, P, P, 128, 128, 64, NULL) == OK

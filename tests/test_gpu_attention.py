@@ -1,0 +1,266 @@
+"""GPU parity of the verify attention (HIP kernels through the C interface) against the fp64
+oracle, on the named workloads at full size and on edge cases."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ring_kv_amd as rk
+from synth import (AttnCase, contig_case, paged_case, paged_store, ring_case, ring_positions,
+                   ring_store, round_f32_to_bf16_bits, stack_layer_kind, workload)
+from gpu_util import (assert_attn_close, dev, run_gpu, run_oracle, say)
+
+pytestmark = pytest.mark.gpu
+
+
+# ---- the named workloads at full size ------------------------------------------------------
+
+def test_contig_1k_f32_all_splits():
+    c, _ = workload("contig_1k_f32")
+    ref = run_oracle(c)
+    for s in (0, 1, 3, 16):
+        say(f"contig_1k_f32 splits={s}")
+        assert_attn_close(run_gpu(c, num_splits=s), ref, "f32", f"contig_1k_f32 S={s}")
+
+
+def test_ring_w512_r2048():
+    c, _ = workload("ring_w512_r2048")
+    ref = run_oracle(c)
+    for s in (0, 1, 3):
+        say(f"ring_w512_r2048 splits={s}")
+        assert_attn_close(run_gpu(c, num_splits=s), ref, "bf16", f"ring S={s}")
+
+
+def test_paged_8k_and_permutation_invariance():
+    c, _ = workload("paged_8k")
+    ref = run_oracle(c)
+    say("paged_8k auto splits")
+    got = run_gpu(c)
+    assert_attn_close(got, ref, "bf16", "paged_8k")
+    # the same context under other pool permutations: bit-identical GPU outputs
+    for perm in ("identity", "reversed"):
+        say(f"paged_8k perm={perm}")
+        c2 = paged_case(3, 0, 8192, 16, 16, 4, 128, n_slots=128, perm=perm)
+        np.testing.assert_array_equal(c2.k_rows, c.k_rows)
+        g2 = run_gpu(c2)
+        np.testing.assert_array_equal(g2[0], got[0])
+        np.testing.assert_array_equal(g2[1], got[1])
+
+
+def test_paged_256k_outliers():
+    c, _ = workload("paged_256k")
+    say("paged_256k: oracle")
+    ref = run_oracle(c)
+    say("paged_256k: gpu auto splits")
+    assert_attn_close(run_gpu(c), ref, "bf16", "paged_256k")
+
+
+@pytest.mark.parametrize("layer", list(range(40)))
+def test_stack_40l_131k_layer(layer):
+    c, _ = workload("stack_40l_131k", layer)
+    assert c.kind == stack_layer_kind(layer)
+    say(f"stack layer {layer} ({c.kind})")
+    assert_attn_close(run_gpu(c), run_oracle(c), "bf16", f"stack layer {layer}")
+
+
+# ---- exact coverage: Q = 0 makes every visible weight exactly 1 -----------------------------
+
+def _one_hot_v(n, first, hkv, d):
+    v = np.zeros((n, hkv, d), np.float32)
+    for g in range(hkv):
+        pos = np.arange(first, first + n)
+        v[np.arange(n), g, (pos // 64 + 3 * g + pos) % d] = 1.0
+    return round_f32_to_bf16_bits(v)
+
+
+def _count(q_pos, window, hq, hkv, d):
+    G = hq // hkv
+    out = np.zeros((len(q_pos), hq, d))
+    lse = np.zeros((len(q_pos), hq))
+    for i, p in enumerate(q_pos):
+        lo = max(0, p - window + 1) if window else 0
+        j = np.arange(lo, p + 1)
+        for h in range(hq):
+            g = h // G
+            np.add.at(out[i, h], (j // 64 + 3 * g + j) % d, 1.0 / len(j))
+            lse[i, h] = math.log(len(j))
+    return out, lse
+
+
+@pytest.mark.parametrize("ctx,splits", [(8192, 0), (8192, 1), (262144, 0), (65, 0), (17, 0),
+                                        (8207, 5)])
+def test_exact_coverage_paged(ctx, splits):
+    hq, hkv, d, q_len = 16, 4, 128, 16
+    nch = -(-ctx // 64)
+    pt = np.random.default_rng(ctx).permutation(nch).astype(np.int32)
+    k = np.zeros((ctx, hkv, d), np.uint16)
+    v = _one_hot_v(ctx, 0, hkv, d)
+    kp, vp = paged_store(k, v, pt, nch)
+    say(f"coverage paged ctx={ctx} splits={splits}")
+    out, lse = rk.verify_attn_paged(dev(np.zeros((q_len, hq, d), np.uint16)), dev(kp), dev(vp),
+                                    dev(pt), ctx, num_splits=splits)
+    eo, el = _count(range(ctx - q_len, ctx), 0, hq, hkv, d)
+    np.testing.assert_allclose(out.cpu().numpy(), eo, rtol=0, atol=2e-6)
+    np.testing.assert_allclose(lse.cpu().numpy(), el, rtol=0, atol=2e-6)
+
+
+@pytest.mark.parametrize("pos0", [30000, 30720, 2040, 100, 0, 131056])
+def test_exact_coverage_ring(pos0):
+    hq, hkv, d, q_len, R, W = 16, 4, 128, 16, 2048, 512
+    first, last = ring_positions(pos0, q_len, R)
+    n = last - first + 1
+    kr, vr = ring_store(np.zeros((n, hkv, d), np.uint16), _one_hot_v(n, first, hkv, d), first, R)
+    say(f"coverage ring pos0={pos0}")
+    out, lse = rk.verify_attn_ring(dev(np.zeros((q_len, hq, d), np.uint16)), dev(kr), dev(vr),
+                                   pos0, W)
+    eo, el = _count(range(pos0, pos0 + q_len), W, hq, hkv, d)
+    np.testing.assert_allclose(out.cpu().numpy(), eo, rtol=0, atol=2e-6)
+    np.testing.assert_allclose(lse.cpu().numpy(), el, rtol=0, atol=2e-6)
+
+
+# ---- ring = contiguous window, at wraps and clips ----------------------------------------------
+
+@pytest.mark.parametrize("pos0", [30720, 2040, 100, 0, 2032])
+def test_ring_positions(pos0):
+    c = ring_case(902, 0, pos0, 16, 16, 4, 128, 2048, 512)
+    say(f"ring pos0={pos0}")
+    assert_attn_close(run_gpu(c), run_oracle(c), "bf16", f"ring pos0={pos0}")
+
+
+def test_ring_small_ring_and_other_windows():
+    for pos0, R, W in ((5000, 640, 600), (777, 128, 100), (64, 64, 49), (10, 2048, 1)):
+        c = ring_case(905, pos0, pos0, 16, 16, 4, 128, R, W)
+        say(f"ring pos0={pos0} R={R} W={W}")
+        assert_attn_close(run_gpu(c), run_oracle(c), "bf16", f"ring R={R} W={W}")
+
+
+# ---- paged edges: ragged tails, block straddling a chunk, splits, shapes -------------------------
+
+@pytest.mark.parametrize("ctx", [16, 17, 63, 64, 65, 127, 8193, 8207])
+def test_paged_ragged(ctx):
+    c = paged_case(906, ctx, ctx, 16, 16, 4, 128, n_slots=-(-ctx // 64) + 3)
+    ref = run_oracle(c)
+    for s in (0, 1, 7):
+        say(f"paged ctx={ctx} splits={s}")
+        assert_attn_close(run_gpu(c, num_splits=s), ref, "bf16", f"paged ctx={ctx} S={s}")
+
+
+@pytest.mark.parametrize("q_len,hq,hkv,d", [(1, 16, 4, 128), (17, 16, 4, 128), (16, 8, 8, 128),
+                                            (16, 32, 4, 128), (32, 32, 4, 128),
+                                            (16, 16, 4, 64), (5, 6, 2, 64)])
+def test_paged_shapes(q_len, hq, hkv, d):
+    c = paged_case(907, q_len * 100 + hq, 3000 + q_len, q_len, hq, hkv, d, n_slots=60)
+    say(f"paged shape q_len={q_len} hq={hq} hkv={hkv} d={d}")
+    assert_attn_close(run_gpu(c), run_oracle(c), "bf16", f"paged shape {q_len},{hq},{hkv},{d}")
+
+
+@pytest.mark.parametrize("q_len,hq,hkv,d", [(1, 16, 4, 128), (17, 16, 4, 128), (16, 16, 4, 64)])
+def test_ring_shapes(q_len, hq, hkv, d):
+    c = ring_case(908, q_len, 20000, q_len, hq, hkv, d, 2048, 512)
+    say(f"ring shape q_len={q_len} hq={hq} hkv={hkv} d={d}")
+    assert_attn_close(run_gpu(c), run_oracle(c), "bf16", f"ring shape {q_len},{hq},{hkv},{d}")
+
+
+def test_paged_long_split_refreshes_page_table():
+    # one split over 2,048 chunks walks the page-table slice refresh path
+    c = paged_case(909, 0, 131072, 16, 16, 4, 128, n_slots=2100)
+    ref = run_oracle(c)
+    for s in (1, 2):
+        say(f"paged 131072 splits={s}")
+        assert_attn_close(run_gpu(c, num_splits=s), ref, "bf16", f"paged long S={s}")
+
+
+def test_paged_out_of_range_entry_contributes_nothing():
+    c = paged_case(910, 0, 4096, 16, 16, 4, 128, n_slots=64)
+    pt = c.page_table.copy()
+    pt[5] = 64           # outside the pool
+    pt[9] = -3
+    say("paged with out-of-range table entries")
+    out, lse = rk.verify_attn_paged(dev(c.q), dev(c.k_pool), dev(c.v_pool), dev(pt), 4096)
+    keep = np.array([j for j in range(4096) if j // 64 not in (5, 9)])
+    kg, vg = oracle.gather_paged(c.k_pool, c.v_pool, c.page_table, keep)
+    ref = oracle.attend_rows(oracle.to_f64(c.q, "bf16"), lambda g: oracle.to_f64(kg(g), "bf16"),
+                             lambda g: oracle.to_f64(vg(g), "bf16"), keep, np.arange(4080, 4096),
+                             0, 1 / math.sqrt(128), 4)
+    torch.cuda.synchronize()
+    assert_attn_close((out.cpu().numpy(), lse.cpu().numpy()), ref, "bf16", "bad entries")
+
+
+# ---- determinism, two-phase form, verify == decode ------------------------------------------------
+
+def test_determinism_and_two_phase():
+    c, _ = workload("paged_8k")
+    q, kp, vp, pt = dev(c.q), dev(c.k_pool), dev(c.v_pool), dev(c.page_table)
+    say("paged_8k determinism")
+    o1, l1 = rk.verify_attn_paged(q, kp, vp, pt, 8192)
+    o2, l2 = rk.verify_attn_paged(q, kp, vp, pt, 8192)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    S = rk.verify_attn_paged_auto_splits(16, 4, 128, 16, 8192)
+    say("paged_8k two-phase")
+    po, pl = rk.verify_attn_paged_partial(q, kp, vp, pt, 8192, S)
+    o3, l3 = rk.attn_merge_partials(po, pl, 16, 16)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+    # the partials themselves against the oracle over each split's keys
+    cps = -(-128 // S)
+    qf = oracle.to_f64(c.q, "bf16")
+    pon, pln = po.cpu().numpy(), pl.cpu().numpy()
+    for s in (0, S // 2, S - 1):
+        keys = np.arange(s * cps * 64, min((s + 1) * cps * 64, 8192))
+        kg, vg = oracle.gather_paged(c.k_pool, c.v_pool, c.page_table, keys)
+        o, l = oracle.attend_rows(qf, lambda g: oracle.to_f64(kg(g), "bf16"),
+                                  lambda g: oracle.to_f64(vg(g), "bf16"), keys,
+                                  np.arange(8176, 8192), 0, 1 / math.sqrt(128), 4)
+        for g in range(4):
+            for r in range(64):
+                i, h = r // 4, g * 4 + r % 4
+                assert np.abs(pon[g, s, r] - o[i, h]).max() <= 1e-2
+                assert abs(pln[g, s, r] - l[i, h]) <= 2e-3
+
+
+def test_verify_row_equals_single_token_decode():
+    c, _ = workload("paged_8k")
+    say("verify vs decode (q_len=1)")
+    full, _ = run_gpu(c)
+    kd, vd = dev(c.k_rows), dev(c.v_rows)
+    kp, vp, pt = dev(c.k_pool), dev(c.v_pool), dev(c.page_table)
+    for i in (0, 7, 15):
+        p = 8192 - 16 + i
+        o1, _ = rk.decode_attn_ref_layout(dev(c.q[i:i + 1]), kd, vd, p + 1)
+        o2, _ = rk.verify_attn_paged(dev(c.q[i:i + 1]), kp, vp, pt, p + 1)
+        torch.cuda.synchronize()
+        assert np.abs(o1.cpu().numpy()[0] - full[i]).max() <= 1e-2
+        assert np.abs(o2.cpu().numpy()[0] - full[i]).max() <= 1e-2
+
+
+def test_contig_bf16_and_window():
+    c = contig_case(911, 0, 3000, 16, 16, 4, 128, "bf16", window=512)
+    say("contig bf16 window 512")
+    assert_attn_close(run_gpu(c), run_oracle(c), "bf16", "contig bf16 W=512")
+    c = contig_case(912, 0, 700, 3, 6, 2, 64, "f32", window=100)
+    say("contig f32 window 100")
+    assert_attn_close(run_gpu(c), run_oracle(c), "f32", "contig f32 W=100")
+
+
+# ---- layout helpers: GPU scatter == the documented layout -----------------------------------------
+
+def test_layout_helpers_bit_exact():
+    c = paged_case(913, 0, 5000, 16, 16, 4, 128, n_slots=90)
+    kp = torch.zeros((90, 4, 64, 128), dtype=torch.bfloat16, device="cuda")
+    vp = torch.zeros((90, 4, 128, 64), dtype=torch.bfloat16, device="cuda")
+    say("ref_layout_to_paged")
+    rk.ref_layout_to_paged(dev(c.k_rows), dev(c.v_rows), 0, kp, vp, dev(c.page_table))
+    want_k, want_v = paged_store(c.k_rows, c.v_rows, c.page_table, 90, fill=np.uint16(0))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(kp.view(torch.int16).cpu().numpy().view(np.uint16), want_k)
+    np.testing.assert_array_equal(vp.view(torch.int16).cpu().numpy().view(np.uint16), want_v)
+    r = ring_case(914, 0, 30720, 16, 16, 4, 128, 2048, 512)
+    kr = torch.zeros((32, 4, 64, 128), dtype=torch.bfloat16, device="cuda")
+    vr = torch.zeros((32, 4, 128, 64), dtype=torch.bfloat16, device="cuda")
+    say("ref_layout_to_ring")
+    rk.ref_layout_to_ring(dev(r.k_rows), dev(r.v_rows), r.rows_first, kr, vr)
+    wk, wv = ring_store(r.k_rows, r.v_rows, r.rows_first, 2048, fill=np.uint16(0))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(kr.view(torch.int16).cpu().numpy().view(np.uint16), wk)
+    np.testing.assert_array_equal(vr.view(torch.int16).cpu().numpy().view(np.uint16), wv)
