@@ -22,6 +22,8 @@
 #include "rkv_device.hpp"
 #include "rkv_launch.hpp"
 
+#include <type_traits>
+
 namespace rkv {
 
 namespace {
@@ -33,8 +35,27 @@ __device__ __forceinline__ int sigma(int tm, int m) {
   return 32 * (tm >> 1) + 8 * (m >> 2) + 4 * (tm & 1) + (m & 3);
 }
 
-__device__ __forceinline__ int swz_k(int key) { return (key & 3) | (((key >> 3) & 1) << 2); }
-__device__ __forceinline__ int swz_v(int d) { return d & 7; }
+// XOR swizzles of the 16-byte pieces inside an LDS row.  A K read of one MFMA operand touches
+// 16 keys (bits 0,1,3,4 of the key vary) at one piece; a V^T read touches 16 consecutive rows
+// d.  The swizzles give every group of 8 lanes 8 distinct 16-byte slots of a 128-byte bank
+// line and every group of 16 lanes 16 distinct slots of a 256-byte line.
+template <int D>
+__device__ __forceinline__ int swz_k(int key) {
+  return D == 128 ? ((key & 3) | ((key >> 1) & 12)) : ((key & 3) | ((key >> 1) & 4));
+}
+__device__ __forceinline__ int swz_v(int d) { return ((d >> 1) & 7) ^ ((d & 1) << 2); }
+
+// Lazy rescaling: a row keeps its running max until a score exceeds it by more than this
+// (exp2 domain), so weights stay below 2^8 and the accumulators are rescaled only rarely.
+constexpr float kRescaleSlack = 8.0f;
+
+// max over the four lanes of a row (lanes n, n+16, n+32, n+48): gfx950 row-swap permutes
+__device__ __forceinline__ float row_max4(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
 constexpr int kPtCap = 512;   // page-table entries kept in LDS (a power of two, >= 512)
 
@@ -46,7 +67,7 @@ struct Tile {
   static constexpr int elems = 2 * 64 * D;     // bf16 elements per LDS buffer
   // LDS offsets in bf16 elements
   __device__ static __forceinline__ int k_off(int key, int piece) {
-    return key * D + ((piece ^ swz_k(key)) << 3);
+    return key * D + ((piece ^ swz_k<D>(key)) << 3);
   }
   __device__ static __forceinline__ int v_off(int d, int piece) {
     return 64 * D + d * 64 + ((piece ^ swz_v(d)) << 3);
@@ -68,27 +89,46 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// PAGED: slots come from the page table; otherwise the store is a ring (slot = c mod n_slots).
-template <int D, int NW, int NBUF, bool PAGED>
-__global__ __launch_bounds__(NW * 64)
+// Template parameters:
+//   NRG    row groups: wave (rg, kh) owns rows 16*rg .. 16*rg+15 of the KV head's rows
+//   KS     key halves: with KS = 2 each chunk's 64 keys are split between two waves per row
+//          group (keys 0..31 and 32..63); each keeps its own online-softmax state and the two
+//          states merge through LDS at the end.  Two waves per SIMD, each with half the
+//          dependent work per chunk.
+//   QLDS   Q comes in through the same direct-to-LDS path as K and V (rows <= 64), so no
+//          compiler-visible load precedes the chunk pipeline
+//   PAGED  slots come from the page table; otherwise the store is a ring (slot = c mod n_slots)
+template <int D, int NRG, int KS, bool QLDS, bool PAGED>
+__global__ __launch_bounds__(NRG * KS * 64)
 void chunk_attn_kernel(ChunkAttnArgs a) {
   using T = Tile<D>;
+  constexpr int NW = NRG * KS;
   constexpr int NT = NW * 64;
+  constexpr int NBUF = 4;
   constexpr int LPC = (T::kPieces + T::vPieces) / NT;   // 16-byte loads per chunk per thread
   static_assert((T::kPieces + T::vPieces) % NT == 0, "pieces must divide evenly");
   static_assert(T::kPieces % 64 == 0, "a wave's load must fall in one tile");
   constexpr int PF = NBUF - 1;                           // chunks in flight ahead of compute
-  static_assert(PF >= 1 && (PF - 1) * LPC < 64, "vmcnt range");
+  static_assert(PF * LPC < 64, "vmcnt range");
   constexpr int KK = D / 32;
   constexpr int TMD = D / 16;
+  constexpr int NKS = KS == 2 ? 1 : 2;                   // 32-key halves per wave per chunk
   constexpr uint32_t kBufBytes = T::elems * 2;
+  constexpr int QP = QLDS ? 64 * D / 8 : 0;              // Q pieces (64 rows)
+  static_assert(!QLDS || NRG * 16 <= 64, "LDS Q holds 64 rows (one row tile)");
+  static_assert(QP % NT == 0, "Q pieces must divide evenly");
+  constexpr int QPT = QP / NT;
+  static_assert(PF * LPC + QPT < 64, "vmcnt range");
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[NBUF][T::elems];
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[QLDS ? 64 * D : 8];
   __shared__ int pt_lds[kPtCap];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = w % NRG;
+  const int kh = w / NRG;
   const int ln = lane & 15;
   const int lq = lane >> 4;
 
@@ -102,21 +142,22 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
   const int64_t c_end = a.c_first + a.n_chunks;
   const int nloc = (int)imax64(0, imin64((int64_t)a.cps, c_end - c_lo));
 
-  // ---- this lane's query row ---------------------------------------------------------
-  const int r = w * 16 + ln;
+  // ---- this lane's query row (row tile blockIdx.y holds rows 16*NRG*y ..) ----------------
+  const int row0 = blockIdx.y * (NRG * 16);
+  const int r = row0 + rg * 16 + ln;
   const bool row_ok = r < rows;
   const int qi = row_ok ? r / G : 0;
   const int hq = g * G + (row_ok ? r % G : 0);
   const int64_t p_i = a.p0 + qi;
   const int64_t lo_i = a.window > 0 ? imax64(0, p_i - a.window + 1) : 0;
-  const bool wave_active = w * 16 < rows;
+  const bool wave_active = row0 + rg * 16 < rows;
   const int64_t p_first = a.p0;
   const int64_t p_last = a.p0 + a.q_len - 1;
   const int64_t lo_last = a.window > 0 ? imax64(0, p_last - a.window + 1) : 0;
 
   // Q^T operand of S^T = K Q^T: lane (ln, lq) holds row ln's dims kk*32 + 8*lq .. +7
   bf16x8 qop[KK];
-  {
+  if constexpr (!QLDS) {
     const uint16_t* qrow = a.q + ((int64_t)qi * a.n_q_heads + hq) * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
@@ -133,10 +174,12 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
   if (paged) {
     for (int e = tid; e < kPtCap && e < nloc; e += NT) pt_lds[e] = a.pt[c_lo + e];
   }
-  // Q and the table slice are in registers / LDS before any chunk load is issued, so the
-  // compiler's own waits for them never cover a chunk load.
+  // Register Q and the table slice are complete before any direct-to-LDS load is issued, so
+  // the compiler's own waits for them never cover one of those loads.
+  if constexpr (!QLDS) {
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(qop[kk]));
+    for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(qop[kk]));
+  }
   lds_barrier();
 
   // ring: slot = logical chunk mod n_slots; a ring span covers at most n_slots + 1 chunks
@@ -179,7 +222,7 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
       const uint32_t m0 = __builtin_amdgcn_readfirstlane(lb + (uint32_t)pw * 16u);
       if (pw < T::kPieces) {
         const int key = P / T::kRow, phys = P % T::kRow;
-        dma16(m0, kb, (uint32_t)(key * T::kRow + (phys ^ swz_k(key))) * 16u);
+        dma16(m0, kb, (uint32_t)(key * T::kRow + (phys ^ swz_k<D>(key))) * 16u);
       } else {
         const int vp = P - T::kPieces;
         const int d = vp >> 3, phys = vp & 7;
@@ -189,11 +232,115 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
   };
 
   // ---- running softmax state ---------------------------------------------------------
-  float m_run = -INFINITY;   // exp2-domain running max of this lane's row
-  float l_run = 0.f;         // this lane's share of the row sum (reduced at the end)
+  // m_run: exp2-domain reference max of this lane's row over the wave's keys.  oacc holds
+  // sum_j p_j V_j^T and lacc the row sum sum_j p_j (computed by the matrix core against a
+  // column of ones, so it uses exactly the bf16 weights the PV product uses).
+  float m_run = -INFINITY;
   f32x4 oacc[TMD];
+  f32x4 lacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int t = 0; t < TMD; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // A operand of the ones column: row 0 of an extra 16-row tile of V^T is all ones
+  const bf16x8 ones_col = __builtin_bit_cast(
+      bf16x8, ln == 0 ? u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u}
+                      : u32x4{0u, 0u, 0u, 0u});
+  const float csc = a.scale_log2;
+
+  // EDGE: some key of the chunk is invisible to some row (causal tail, window start) or lies
+  // outside the stored range; interior chunks run without any masking code.
+  auto compute_body = [&](const uint16_t* buf, int64_t cbase, bool partial, auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
+    f32x4 sacc[2 * NKS];
+#pragma unroll
+    for (int j = 0; j < 2 * NKS; ++j) sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      bf16x8 ka[2 * NKS];
+#pragma unroll
+      for (int j = 0; j < 2 * NKS; ++j) {
+        const int tm = 2 * (KS == 2 ? kh : (j >> 1)) + (j & 1);
+        ka[j] = *reinterpret_cast<const bf16x8*>(buf + T::k_off(sigma(tm, ln), 4 * kk + lq));
+      }
+#pragma unroll
+      for (int j = 0; j < 2 * NKS; ++j) sacc[j] = mfma_16x16x32(ka[j], qop[kk], sacc[j]);
+    }
+    // key index within the chunk of score (j, i): 32*ks + 8*lq + 4*(j&1) + i
+    float mx = -INFINITY;
+    if constexpr (EDGE) {
+      // visible keys of this row: [vis_lo, vis_hi] relative to the chunk, clamped to 32 bits
+      const int64_t lo = imax64(lo_i, a.valid_lo) - cbase;
+      const int64_t hi = imin64(p_i, a.valid_hi - 1) - cbase;
+      const int vis_lo = (int)imax64(-1, imin64(lo, 64));
+      const int vis_hi = row_ok ? (int)imax64(-1, imin64(hi, 64)) : -1;
+#pragma unroll
+      for (int j = 0; j < 2 * NKS; ++j) {
+        const int ks = KS == 2 ? kh : (j >> 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kidx = 32 * ks + 8 * lq + 4 * (j & 1) + i;
+          // selection, not arithmetic: a key outside the stored range may hold anything
+          if (kidx < vis_lo || kidx > vis_hi) sacc[j][i] = -INFINITY;
+          mx = fmaxf(mx, sacc[j][i]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2 * NKS; ++j)
+        mx = fmaxf(mx, fmaxf(fmaxf(sacc[j][0], sacc[j][1]), fmaxf(sacc[j][2], sacc[j][3])));
+    }
+    const float t_max = row_max4(mx) * csc;          // scale > 0: max commutes with it
+    // rescale only when some row's max passed its reference by more than the slack
+    const bool grow = t_max > m_run + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? t_max : m_run;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;   // -inf -> 0
+#pragma unroll
+      for (int t = 0; t < TMD; ++t) oacc[t] *= alpha;
+      lacc *= alpha;
+      m_run = m_new;
+    }
+    // a row with no visible key yet keeps m_run = -inf; its weights must come out 0, not NaN
+    const float m_use = (EDGE && m_run == -INFINITY) ? 0.f : m_run;
+    uint32_t pw[NKS][4];   // P^T operand words per 32-key half
+#pragma unroll
+    for (int h = 0; h < NKS; ++h) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int j = 2 * h + hh;
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[j][0], csc, -m_use));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[j][1], csc, -m_use));
+        const float p2 = __builtin_amdgcn_exp2f(fmaf(sacc[j][2], csc, -m_use));
+        const float p3 = __builtin_amdgcn_exp2f(fmaf(sacc[j][3], csc, -m_use));
+        pw[h][2 * hh] = pack_bf16x2(p0, p1);
+        pw[h][2 * hh + 1] = pack_bf16x2(p2, p3);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < NKS; ++h) {
+      const int ks = KS == 2 ? kh : h;
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pw[h][0], pw[h][1], pw[h][2], pw[h][3]});
+      uint32_t vmask[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+      if constexpr (EDGE) {
+        // keys outside the stored range: zero their V so that 0 * (anything) stays 0
+        if (partial) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int64_t jj = cbase + 32 * ks + 8 * lq + e;
+            if (jj < a.valid_lo || jj >= a.valid_hi) vmask[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+          }
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < TMD; ++t) {
+        u32x4 raw = *reinterpret_cast<const u32x4*>(buf + T::v_off(16 * t + ln, 4 * ks + lq));
+        if constexpr (EDGE) {
+          raw[0] &= vmask[0]; raw[1] &= vmask[1]; raw[2] &= vmask[2]; raw[3] &= vmask[3];
+        }
+        oacc[t] = mfma_16x16x32(__builtin_bit_cast(bf16x8, raw), pb, oacc[t]);
+      }
+      lacc = mfma_16x16x32(ones_col, pb, lacc);
+    }
+  };
 
   auto compute = [&](const uint16_t* buf, int loc) {
     if (!wave_active) return;
@@ -201,91 +348,45 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
     const int64_t cbase = (c_lo + loc) * 64;
     const bool partial = cbase < a.valid_lo || cbase + 64 > a.valid_hi;
     const bool edge = (cbase + 63 > p_first) || (cbase < lo_last) || partial;
-    // four independent 16-key tiles per k-step keep the matrix pipe busy
-    f32x4 sacc[4];
-#pragma unroll
-    for (int tm = 0; tm < 4; ++tm) sacc[tm] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      bf16x8 ka[4];
-#pragma unroll
-      for (int tm = 0; tm < 4; ++tm)
-        ka[tm] = *reinterpret_cast<const bf16x8*>(buf + T::k_off(sigma(tm, ln), 4 * kk + lq));
-#pragma unroll
-      for (int tm = 0; tm < 4; ++tm) sacc[tm] = mfma_16x16x32(ka[tm], qop[kk], sacc[tm]);
-    }
-    float sc[4][4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int tm = 0; tm < 4; ++tm) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float t = sacc[tm][i] * a.scale_log2;
-        if (edge) {
-          // selection, not arithmetic: a key outside the stored range may hold anything
-          const int64_t j = cbase + 32 * (tm >> 1) + 8 * lq + 4 * (tm & 1) + i;
-          if (!row_ok || j < lo_i || j > p_i) t = -INFINITY;
-        }
-        sc[tm][i] = t;
-        mx = fmaxf(mx, t);
-      }
-    }
-    mx = fmaxf(mx, wave_xor(mx, 16));
-    mx = fmaxf(mx, wave_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
-    uint32_t pw[2][4];   // P^T operand words for ks = 0, 1
-    float lsum = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int tm = 2 * ks + hh;
-        const float p0 = __builtin_amdgcn_exp2f(sc[tm][0] - m_use);
-        const float p1 = __builtin_amdgcn_exp2f(sc[tm][1] - m_use);
-        const float p2 = __builtin_amdgcn_exp2f(sc[tm][2] - m_use);
-        const float p3 = __builtin_amdgcn_exp2f(sc[tm][3] - m_use);
-        const uint32_t w01 = pack_bf16x2(p0, p1);
-        const uint32_t w23 = pack_bf16x2(p2, p3);
-        pw[ks][2 * hh] = w01;
-        pw[ks][2 * hh + 1] = w23;
-        // the row sum uses the same rounded weights the PV product sees
-        lsum += __uint_as_float(w01 << 16) + __uint_as_float(w01 & 0xffff0000u) +
-                __uint_as_float(w23 << 16) + __uint_as_float(w23 & 0xffff0000u);
-      }
-    }
-    l_run = l_run * alpha + lsum;
-#pragma unroll
-    for (int t = 0; t < TMD; ++t) oacc[t] *= alpha;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pw[ks][0], pw[ks][1], pw[ks][2], pw[ks][3]});
-      // keys outside the stored range: zero their V so that 0 * (anything) stays 0
-      uint32_t vmask[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
-      if (partial) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int64_t j = cbase + 32 * ks + 8 * lq + e;
-          if (j < a.valid_lo || j >= a.valid_hi) vmask[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < TMD; ++t) {
-        u32x4 raw = *reinterpret_cast<const u32x4*>(buf + T::v_off(16 * t + ln, 4 * ks + lq));
-        if (partial) {
-          raw[0] &= vmask[0]; raw[1] &= vmask[1]; raw[2] &= vmask[2]; raw[3] &= vmask[3];
-        }
-        oacc[t] = mfma_16x16x32(__builtin_bit_cast(bf16x8, raw), pb, oacc[t]);
-      }
-    }
+    if (edge)
+      compute_body(buf, cbase, partial, std::true_type{});
+    else
+      compute_body(buf, cbase, partial, std::false_type{});
   };
 
-  // ---- pipeline: PF chunks in flight while one is computed -----------------------------
+  // ---- pipeline: Q, then PF chunks in flight while one is computed ---------------------
+  if constexpr (QLDS) {
+    if (nloc > 0) {
+      // Q rows of this KV head, row r = i*G + (h - g*G) at LDS row r; rows past the last are
+      // loaded from row 0 (any valid address) and never written out
+      const uint32_t qb = (uint32_t)(uintptr_t)&q_lds[0];
+#pragma unroll
+      for (int u = 0; u < QPT; ++u) {
+        const int pw = u * NT + w * 64;
+        const int P = pw + lane;
+        const int rr = P / (D / 8), pc = P % (D / 8);
+        const int rs = rr < rows ? rr : 0;
+        const int64_t qoff = (((int64_t)(rs / G) * a.n_q_heads + g * G + rs % G) * D + pc * 8) * 2;
+        dma16(__builtin_amdgcn_readfirstlane(qb + (uint32_t)pw * 16u), a.q, (uint32_t)qoff);
+      }
+    }
+  }
 #pragma unroll
   for (int k = 0; k < PF; ++k)
     if (k < nloc) issue(k);
+  if constexpr (QLDS) {
+    if (nloc > 0) {
+      // wait for Q alone (the chunks issued after it stay in flight)
+      const int after = nloc < PF ? nloc : PF;
+      if (after >= 3) wait_vmcnt<3 * LPC>();
+      else if (after == 2) wait_vmcnt<2 * LPC>();
+      else wait_vmcnt<LPC>();
+      lds_barrier();
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        qop[kk] = *reinterpret_cast<const bf16x8*>(&q_lds[r * D + kk * 32 + lq * 8]);
+    }
+  }
 
   for (int loc = 0; loc < nloc; ++loc) {
     // chunks issued after this one: min(PF-1, nloc-1-loc); wait until only they are in flight
@@ -301,11 +402,42 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
   }
 
   // ---- epilogue ------------------------------------------------------------------------
-  if (!wave_active) return;
-  float l = l_run;
-  l += wave_xor(l, 16);
-  l += wave_xor(l, 32);
-  if (!row_ok) return;
+  // row sum: component 0 of lacc in lane ln (lane group 0); every lane of the row needs it
+  float l = __shfl(lacc[0], ln, kWave);
+  if constexpr (KS == 2) {
+    // key half 1 hands (m, l, O) to key half 0 through LDS; every chunk load has landed
+    float* xo = reinterpret_cast<float*>(&lds[0][0]);          // [NRG][16][D]
+    float* xm = xo + NRG * 16 * D;                               // [NRG][16]
+    float* xl = xm + NRG * 16;
+    lds_barrier();
+    if (kh == 1 && wave_active) {
+#pragma unroll
+      for (int t = 0; t < TMD; ++t)
+        *reinterpret_cast<f32x4*>(&xo[(rg * 16 + ln) * D + 16 * t + 4 * lq]) = oacc[t];
+      if (lq == 0) {
+        xm[rg * 16 + ln] = m_run;
+        xl[rg * 16 + ln] = l;
+      }
+    }
+    lds_barrier();
+    if (kh == 1) return;
+    if (wave_active) {
+      const float m1 = xm[rg * 16 + ln];
+      const float l1 = xl[rg * 16 + ln];
+      const float M = fmaxf(m_run, m1);
+      const float Mu = M == -INFINITY ? 0.f : M;
+      const float a0 = __builtin_amdgcn_exp2f(m_run - Mu);
+      const float a1 = __builtin_amdgcn_exp2f(m1 - Mu);
+      l = a0 * l + a1 * l1;
+#pragma unroll
+      for (int t = 0; t < TMD; ++t) {
+        const f32x4 o1 = *reinterpret_cast<const f32x4*>(&xo[(rg * 16 + ln) * D + 16 * t + 4 * lq]);
+        oacc[t] = oacc[t] * a0 + o1 * a1;
+      }
+      m_run = M;
+    }
+  }
+  if (!wave_active || !row_ok) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
   const float lse_nat = l > 0.f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
   float* dst;
@@ -324,23 +456,25 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
   }
 }
 
-template <int D, int NW>
+template <int D, int NRG, int KS, bool QLDS>
 hipError_t launch_t(const ChunkAttnArgs& a, hipStream_t stream) {
-  const int blocks = a.n_kv_heads * a.num_splits;
-  // four LDS chunk buffers (3 chunks in flight); D = 128 uses 128 KiB + the table slice
+  const int rows = a.q_len * a.G;
+  const dim3 blocks(a.n_kv_heads * a.num_splits, (rows + NRG * 16 - 1) / (NRG * 16));
+  const dim3 threads(NRG * KS * 64);
   if (a.pt != nullptr)
-    hipLaunchKernelGGL((chunk_attn_kernel<D, NW, 4, true>), dim3(blocks), dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((chunk_attn_kernel<D, NRG, KS, QLDS, true>), blocks, threads, 0, stream, a);
   else
-    hipLaunchKernelGGL((chunk_attn_kernel<D, NW, 4, false>), dim3(blocks), dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((chunk_attn_kernel<D, NRG, KS, QLDS, false>), blocks, threads, 0, stream, a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const ChunkAttnArgs& a, hipStream_t stream) {
   const int rows = a.q_len * a.G;
-  if (rows <= 64) return launch_t<D, 4>(a, stream);
-  if (rows <= 128) return launch_t<D, 8>(a, stream);
-  return launch_t<D, 16>(a, stream);
+  // up to 64 rows: one row tile, two waves per row group (key halves), Q through LDS;
+  // more rows: tiles of 128 rows (blockIdx.y), eight waves without key split
+  if (rows <= 64) return launch_t<D, 4, 2, true>(a, stream);
+  return launch_t<D, 8, 1, false>(a, stream);
 }
 
 }  // namespace

@@ -8,7 +8,12 @@
 namespace rkv {
 namespace {
 
-// one workgroup per (KV head, row); one thread per output dimension
+// One workgroup per (KV head, row), one thread per output dimension.  The splits are read in
+// tiles of kTile with every load of a tile in flight at once (a split-by-split loop would wait
+// one memory latency per split), and merged online: the running max only ever grows, and the
+// running sums are rescaled when it does.
+constexpr int kTile = 16;
+
 __global__ __launch_bounds__(128) void merge_kernel(MergeArgs a) {
   const int rows = a.q_len * a.G;
   const int g = blockIdx.x / rows;
@@ -19,18 +24,32 @@ __global__ __launch_bounds__(128) void merge_kernel(MergeArgs a) {
   const float* po = a.part_o + ((int64_t)g * S * rows + r) * a.head_dim + d;
   const int64_t ostride = (int64_t)rows * a.head_dim;
 
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, lse[(int64_t)s * rows]);
-  float sum = 0.f, acc = 0.f;
-  if (M > -INFINITY) {
-    for (int s = 0; s < S; ++s) {
-      const float ls = lse[(int64_t)s * rows];
-      if (ls > -INFINITY) {
-        const float w = expf(ls - M);
-        sum += w;
-        acc += w * po[s * ostride];
-      }
+  float M = -INFINITY, sum = 0.f, acc = 0.f;
+  for (int s0 = 0; s0 < S; s0 += kTile) {
+    float ls[kTile], ov[kTile];
+#pragma unroll
+    for (int j = 0; j < kTile; ++j) {
+      // clamped index: every load is issued unconditionally, the tail is masked afterwards
+      const int sj = min(s0 + j, S - 1);
+      const float l = lse[(int64_t)sj * rows];
+      const float o = po[sj * ostride];
+      ls[j] = s0 + j < S ? l : -INFINITY;
+      ov[j] = o;
     }
+    float mt = M;
+#pragma unroll
+    for (int j = 0; j < kTile; ++j) mt = fmaxf(mt, ls[j]);
+    if (mt == -INFINITY) continue;           // no split so far saw a key of this row
+    const float rescale = expf(M - mt);      // M = -inf: 0, and sum = acc = 0 anyway
+    sum *= rescale;
+    acc *= rescale;
+#pragma unroll
+    for (int j = 0; j < kTile; ++j) {
+      const float w = ls[j] > -INFINITY ? expf(ls[j] - mt) : 0.f;
+      sum += w;
+      acc = fmaf(w, ov[j], acc);
+    }
+    M = mt;
   }
   const int qi = r / a.G;
   const int h = g * a.G + r % a.G;
