@@ -100,7 +100,7 @@ class Stack:
                                     dtype=torch.uint8, device="cuda")
         self.ws_ring = torch.empty(max(1, L.verify_attn_ring_workspace_bytes(ctypes.byref(dims), 2048, 512, 0)),
                                    dtype=torch.uint8, device="cuda")
-        self.ws_acc = torch.empty(L.verify_accept_workspace_bytes(16, 65536), dtype=torch.uint8, device="cuda")
+        self.ws_acc = torch.zeros(L.verify_accept_workspace_bytes(16, 65536), dtype=torch.uint8, device="cuda")
         self.splits = rk.verify_attn_paged_auto_splits(16, 4, 128, 16, 131072)
         self.part_o = torch.empty((4, self.splits, 64, 128), dtype=torch.float32, device="cuda")
         self.part_l = torch.empty((4, self.splits, 64), dtype=torch.float32, device="cuda")

@@ -1,10 +1,11 @@
 // Greedy acceptance (lucebox post "Laguna XS 2.1 33B on a RTX 3090: 296 tok/s peak, 152 tok/s
 // at 256K context", "TL;DR" and "The model, fast MoE with a drafter in the box": proposals are
 // verified in one batched forward and only tokens the target itself would emit are
-// committed).  Pass 1: per (row, vocabulary part) the first maximum, reduced within a wave by
-// shuffles and across waves through LDS.  Pass 2 (one workgroup): the row argmaxes, the first
-// disagreement with the draft, and the committed tokens.  Ties go to the lower index, values
-// compare as float32 (-0 == +0).
+// committed).  One launch: every workgroup finds the first maximum of one (row, vocabulary
+// part), reduced within a wave by shuffles and across waves through LDS, publishes it, and
+// takes a ticket; the workgroup that takes the last ticket reduces the parts to the row
+// argmaxes, finds the first disagreement with the draft, writes the committed tokens and
+// resets the ticket.  Ties go to the lower index, values compare as float32 (-0 == +0).
 #include <limits.h>
 
 #include "rkv_device.hpp"
@@ -28,9 +29,12 @@ __device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
 }
 
 template <bool VEC4>
-__global__ __launch_bounds__(256) void accept_partial_kernel(AcceptArgs a) {
+__global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
   __shared__ float sv[4];
   __shared__ int si[4];
+  __shared__ int last;
+  __shared__ int t[256];
+  __shared__ int acc_len;
   const int row = blockIdx.y, part = blockIdx.x, tid = threadIdx.x;
   const int start = part * a.part_len;
   const int end = min(start + a.part_len, a.vocab);
@@ -61,25 +65,27 @@ __global__ __launch_bounds__(256) void accept_partial_kernel(AcceptArgs a) {
       if (better(sv[k], si[k], bv, bi)) { bv = sv[k]; bi = si[k]; }
     a.part_val[(int64_t)row * a.parts + part] = bv;
     a.part_idx[(int64_t)row * a.parts + part] = bi;
+    // release: this part is visible device-wide before the ticket is taken
+    __threadfence();
+    const unsigned total = (unsigned)(a.parts * a.n_rows);
+    last = atomicAdd(a.ticket, 1u) == total - 1;
   }
-}
-
-__global__ __launch_bounds__(256) void accept_final_kernel(AcceptArgs a) {
-  __shared__ int t[256];
-  __shared__ int acc_len;
-  const int tid = threadIdx.x;
+  __syncthreads();
+  if (!last) return;
+  // acquire: every other workgroup's part is visible to this one
+  __threadfence();
   const int n_draft = a.n_rows - 1;
   if (tid < a.n_rows) {
-    float bv = -INFINITY;
-    int bi = INT_MAX;
+    float rv = -INFINITY;
+    int ri = INT_MAX;
     for (int p = 0; p < a.parts; ++p) {
-      const float v = a.part_val[(int64_t)tid * a.parts + p];
-      const int i = a.part_idx[(int64_t)tid * a.parts + p];
-      if (better(v, i, bv, bi)) { bv = v; bi = i; }
+      const float v = __builtin_nontemporal_load(&a.part_val[(int64_t)tid * a.parts + p]);
+      const int i = __builtin_nontemporal_load(&a.part_idx[(int64_t)tid * a.parts + p]);
+      if (better(v, i, rv, ri)) { rv = v; ri = i; }
     }
-    if (bi == INT_MAX) bi = 0;   // a row of NaNs only: any in-range index
-    t[tid] = bi;
-    if (a.row_argmax != nullptr) a.row_argmax[tid] = bi;
+    if (ri == INT_MAX) ri = 0;   // a row of NaNs only: any in-range index
+    t[tid] = ri;
+    if (a.row_argmax != nullptr) a.row_argmax[tid] = ri;
   }
   __syncthreads();
   if (tid == 0) {
@@ -88,6 +94,7 @@ __global__ __launch_bounds__(256) void accept_final_kernel(AcceptArgs a) {
       if (t[r] != a.proposals[r]) { acc = r; break; }
     acc_len = acc;
     a.accept_len[0] = acc;
+    *a.ticket = 0u;             // ready for the next call
   }
   __syncthreads();
   const int acc = acc_len;
@@ -99,12 +106,9 @@ __global__ __launch_bounds__(256) void accept_final_kernel(AcceptArgs a) {
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream) {
   const dim3 grid(a.parts, a.n_rows);
   if ((a.vocab & 3) == 0 && (a.part_len & 3) == 0)
-    hipLaunchKernelGGL(accept_partial_kernel<true>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(accept_kernel<true>, grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(accept_partial_kernel<false>, grid, dim3(256), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(accept_final_kernel, dim3(1), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(accept_kernel<false>, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -8,61 +8,96 @@
 namespace rkv {
 namespace {
 
-// One workgroup per (KV head, row), one thread per output dimension.  The splits are read in
-// tiles of kTile with every load of a tile in flight at once (a split-by-split loop would wait
-// one memory latency per split), and merged online: the running max only ever grows, and the
-// running sums are rescaled when it does.
-constexpr int kTile = 16;
+// One workgroup of 256 threads per (KV head, row).  Thread (sg, d4) owns four consecutive
+// output dimensions and the splits sg, sg + SG, ...; its first kPre partial vectors are
+// requested before anything else so that the whole merge costs about one memory round trip.
+// The max over the splits' lse values is reduced through LDS, then every thread weighs its
+// splits, and the SG split groups are summed through LDS.
+constexpr int kMergeThreads = 256;
+constexpr int kPre = 8;
 
-__global__ __launch_bounds__(128) void merge_kernel(MergeArgs a) {
+__device__ __forceinline__ float block_max(float v, float* red) {
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  v = red[0];
+  for (int k = 1; k < kMergeThreads / 64; ++k) v = fmaxf(v, red[k]);
+  return v;
+}
+
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
+  constexpr int PR = D / 4;                 // float4 per row
+  constexpr int SG = kMergeThreads / PR;    // split groups
+  __shared__ float red[kMergeThreads / 64];
+  __shared__ f32x4 xacc[SG][PR];
+  __shared__ float xl[SG];
+
   const int rows = a.q_len * a.G;
   const int g = blockIdx.x / rows;
   const int r = blockIdx.x % rows;
-  const int d = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int sg = tid / PR;
+  const int d4 = (tid % PR) * 4;
   const int S = a.num_splits;
   const float* lse = a.part_lse + (int64_t)g * S * rows + r;
-  const float* po = a.part_o + ((int64_t)g * S * rows + r) * a.head_dim + d;
-  const int64_t ostride = (int64_t)rows * a.head_dim;
+  const float* po = a.part_o + ((int64_t)g * S * rows + r) * D + d4;
+  const int64_t ostride = (int64_t)rows * D;
 
-  float M = -INFINITY, sum = 0.f, acc = 0.f;
-  for (int s0 = 0; s0 < S; s0 += kTile) {
-    float ls[kTile], ov[kTile];
+  f32x4 ov[kPre];
+  float lv[kPre];
 #pragma unroll
-    for (int j = 0; j < kTile; ++j) {
-      // clamped index: every load is issued unconditionally, the tail is masked afterwards
-      const int sj = min(s0 + j, S - 1);
-      const float l = lse[(int64_t)sj * rows];
-      const float o = po[sj * ostride];
-      ls[j] = s0 + j < S ? l : -INFINITY;
-      ov[j] = o;
-    }
-    float mt = M;
+  for (int u = 0; u < kPre; ++u) {
+    const int sj = min(sg + SG * u, S - 1);     // clamped: every load is in range and issued
+    ov[u] = *reinterpret_cast<const f32x4*>(po + sj * ostride);
+    lv[u] = lse[(int64_t)sj * rows];
+  }
+  float mloc = -INFINITY;
+  for (int s = tid; s < S; s += kMergeThreads) mloc = fmaxf(mloc, lse[(int64_t)s * rows]);
+  const float M = block_max(mloc, red);
+  const float Mu = M == -INFINITY ? 0.f : M;      // no split saw a key: everything weighs 0
+
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
 #pragma unroll
-    for (int j = 0; j < kTile; ++j) mt = fmaxf(mt, ls[j]);
-    if (mt == -INFINITY) continue;           // no split so far saw a key of this row
-    const float rescale = expf(M - mt);      // M = -inf: 0, and sum = acc = 0 anyway
-    sum *= rescale;
-    acc *= rescale;
-#pragma unroll
-    for (int j = 0; j < kTile; ++j) {
-      const float w = ls[j] > -INFINITY ? expf(ls[j] - mt) : 0.f;
-      sum += w;
-      acc = fmaf(w, ov[j], acc);
-    }
-    M = mt;
+  for (int u = 0; u < kPre; ++u) {
+    const int s = sg + SG * u;
+    const float w = (s < S && lv[u] > -INFINITY) ? expf(lv[u] - Mu) : 0.f;
+    acc += ov[u] * w;
+    L += w;
+  }
+  for (int s = sg + SG * kPre; s < S; s += SG) {
+    const float ls = lse[(int64_t)s * rows];
+    const float w = ls > -INFINITY ? expf(ls - Mu) : 0.f;
+    acc += *reinterpret_cast<const f32x4*>(po + s * ostride) * w;
+    L += w;
+  }
+  xacc[sg][tid % PR] = acc;
+  if (tid % PR == 0) xl[sg] = L;
+  __syncthreads();
+  if (sg != 0) return;
+  float Lt = 0.f;
+  for (int k = 0; k < SG; ++k) {
+    Lt += xl[k];
+    if (k) acc += xacc[k][tid % PR];
   }
   const int qi = r / a.G;
   const int h = g * a.G + r % a.G;
-  a.out[((int64_t)qi * a.n_q_heads + h) * a.head_dim + d] = sum > 0.f ? acc / sum : 0.f;
-  if (a.lse != nullptr && d == 0)
-    a.lse[(int64_t)qi * a.n_q_heads + h] = sum > 0.f ? M + logf(sum) : -INFINITY;
+  *reinterpret_cast<f32x4*>(a.out + ((int64_t)qi * a.n_q_heads + h) * D + d4) =
+      Lt > 0.f ? acc * (1.f / Lt) : f32x4{0.f, 0.f, 0.f, 0.f};
+  if (a.lse != nullptr && d4 == 0)
+    a.lse[(int64_t)qi * a.n_q_heads + h] = Lt > 0.f ? M + logf(Lt) : -INFINITY;
 }
 
 }  // namespace
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
   const int blocks = a.n_kv_heads * a.q_len * a.G;
-  hipLaunchKernelGGL(merge_kernel, dim3(blocks), dim3(a.head_dim), 0, stream, a);
+  if (a.head_dim == 128)
+    hipLaunchKernelGGL(merge_kernel<128>, dim3(blocks), dim3(kMergeThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(merge_kernel<64>, dim3(blocks), dim3(kMergeThreads), 0, stream, a);
   return hipGetLastError();
 }
 
