@@ -122,9 +122,8 @@ int32_t decode_attn_ref_layout(const rkv_attn_dims* dims, const void* q, const v
  * block's own rows included.  k_ring [ring_size/64][Hkv][64][D], v_ring
  * [ring_size/64][Hkv][D][64], bf16; Q bf16.  Slots holding no position may contain
  * anything (they are masked and never multiply a result).
- * num_splits = 0 (the default) runs the window in one launch with every chunk of the span
- * in flight at once and needs no workspace; num_splits >= 1 runs the split-K kernel over
- * that many chunk ranges plus the log-sum-exp merge, with a workspace.
+ * The span of the window is split into num_splits ranges of whole chunks (0: one chunk
+ * per range, every chunk in flight at once) whose partials a log-sum-exp merge combines.
  * ------------------------------------------------------------------------------- */
 size_t verify_attn_ring_workspace_bytes(const rkv_attn_dims* dims, int32_t ring_size,
                                         int32_t window, int32_t num_splits);
@@ -197,8 +196,7 @@ int32_t attn_merge_partials(const rkv_attn_dims* dims, int32_t num_splits,
  *   committed  [n_draft+1] int32 <- proposals[0..a) then t_a; entries after a are -1
  *   row_argmax [n_draft+1] int32 <- t_r (may be NULL)
  * 0 <= n_draft <= 255, vocab >= 1.  NaN logits give an unspecified (but in-range)
- * result.  The workspace holds a completion counter: zero-fill it once when it is
- * allocated; every call leaves it zero again.  Calls sharing a workspace must not overlap.
+ * result.  Calls sharing a workspace must not overlap.
  * ------------------------------------------------------------------------------- */
 size_t verify_accept_workspace_bytes(int32_t n_draft, int32_t vocab);
 int32_t verify_accept(const float* logits, int32_t n_draft, int32_t vocab,

@@ -205,10 +205,7 @@ def verify_accept(logits, proposals, *, accept_len=None, committed=None, row_arg
     if row_argmax is None and want_argmax:
         row_argmax = torch.empty(k + 1, dtype=torch.int32, device=dev)
     L = lib()
-    nbytes = L.verify_accept_workspace_bytes(k, vocab)
-    if workspace is None:
-        workspace = torch.zeros(nbytes, dtype=torch.uint8, device=dev)   # counter starts at 0
-    ws, wsb = _workspace(nbytes, dev, workspace)
+    ws, wsb = _workspace(L.verify_accept_workspace_bytes(k, vocab), dev, workspace)
     check("verify_accept", L.verify_accept(
         _ptr(logits), k, vocab, _ptr(proposals), _ptr(accept_len), _ptr(committed),
         _ptr(row_argmax), _ptr(ws), wsb, _stream(stream, dev)))

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libring_kv.so")
-SOURCES = ["abi.hip", "attn_chunked.hip", "attn_ring.hip", "attn_merge.hip", "attn_contig.hip", "accept.hip",
+SOURCES = ["abi.hip", "attn_chunked.hip", "attn_merge.hip", "attn_contig.hip", "accept.hip",
            "layout.hip"]
 ARCH = "gfx950"
 

@@ -246,7 +246,6 @@ static int64_t ring_max_chunks(const rkv_attn_dims* d, int32_t window) {
 size_t verify_attn_ring_workspace_bytes(const rkv_attn_dims* dims, int32_t ring_size,
                                         int32_t window, int32_t num_splits) {
   if (check_dims(dims) != RKV_OK || window < 1 || num_splits < 0 || ring_size < kChunk) return 0;
-  if (num_splits == 0) return 0;          // one-launch path: no partials
   int32_t s, cps;
   choose_splits(ring_max_chunks(dims, window), dims->n_kv_heads, num_splits, &s, &cps);
   return partial_bytes(dims, s);
@@ -263,12 +262,10 @@ int32_t verify_attn_ring(const rkv_attn_dims* dims, const void* q, const void* k
   if (num_splits < 0) return RKV_ERR_ARG;
   int64_t c_first, n_chunks;
   ring_range(dims, pos0, window, &c_first, &n_chunks);
-  int32_t s = 1, cps = (int32_t)n_chunks;
-  if (num_splits > 0) {
-    split_within(n_chunks, ring_max_chunks(dims, window), dims->n_kv_heads, num_splits, &s, &cps);
-    if (s > 1 && (workspace == nullptr || workspace_bytes < partial_bytes(dims, s)))
-      return RKV_ERR_WORKSPACE;
-  }
+  int32_t s, cps;
+  split_within(n_chunks, ring_max_chunks(dims, window), dims->n_kv_heads, num_splits, &s, &cps);
+  if (s > 1 && (workspace == nullptr || workspace_bytes < partial_bytes(dims, s)))
+    return RKV_ERR_WORKSPACE;
   ChunkAttnArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k_ring);
@@ -290,12 +287,6 @@ int32_t verify_attn_ring(const rkv_attn_dims* dims, const void* q, const void* k
   a.cps = cps;
   a.num_splits = s;
   a.scale_log2 = scale_log2(dims);
-  if (num_splits == 0) {
-    // a window is latency-bound: one launch, every chunk of the span in flight at once
-    a.out = out;
-    a.lse = lse;
-    return hip_status(rkv::launch_ring_attn(a, static_cast<hipStream_t>(stream)));
-  }
   return run_chunk_attn(a, dims, workspace, out, lse, static_cast<hipStream_t>(stream));
 }
 
@@ -387,7 +378,7 @@ size_t verify_accept_workspace_bytes(int32_t n_draft, int32_t vocab) {
   int32_t parts, pl;
   accept_parts(vocab, &parts, &pl);
   const size_t n = (size_t)(n_draft + 1) * parts;
-  return align_up(n * sizeof(float)) + align_up(n * sizeof(int32_t)) + kAlign;   // + ticket
+  return align_up(n * sizeof(float)) + align_up(n * sizeof(int32_t));
 }
 
 int32_t verify_accept(const float* logits, int32_t n_draft, int32_t vocab,
@@ -411,8 +402,6 @@ int32_t verify_accept(const float* logits, int32_t n_draft, int32_t vocab,
   const size_t n = (size_t)a.n_rows * a.parts;
   a.part_val = static_cast<float*>(workspace);
   a.part_idx = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + align_up(n * sizeof(float)));
-  a.ticket = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + align_up(n * sizeof(float)) +
-                                         align_up(n * sizeof(int32_t)));
   return hip_status(rkv::launch_accept(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -1,11 +1,12 @@
 // Greedy acceptance (lucebox post "Laguna XS 2.1 33B on a RTX 3090: 296 tok/s peak, 152 tok/s
 // at 256K context", "TL;DR" and "The model, fast MoE with a drafter in the box": proposals are
 // verified in one batched forward and only tokens the target itself would emit are
-// committed).  One launch: every workgroup finds the first maximum of one (row, vocabulary
-// part), reduced within a wave by shuffles and across waves through LDS, publishes it, and
-// takes a ticket; the workgroup that takes the last ticket reduces the parts to the row
-// argmaxes, finds the first disagreement with the draft, writes the committed tokens and
-// resets the ticket.  Ties go to the lower index, values compare as float32 (-0 == +0).
+// committed).  Pass 1: every workgroup finds the first maximum of one (row, vocabulary part),
+// reduced within a wave by shuffles and across waves through LDS.  Pass 2 (one workgroup):
+// the parts reduce to the row argmaxes, then the first disagreement with the draft and the
+// committed tokens.  Ties go to the lower index, values compare as float32 (-0 == +0).
+// (A single launch that lets the last workgroup finish needs a device-scope release from
+// every workgroup, which costs more here than the second launch.)
 #include <limits.h>
 
 #include "rkv_device.hpp"
@@ -28,32 +29,44 @@ __device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
   }
 }
 
+constexpr int kScan = 16;   // elements per thread per part: part_len <= 256 * kScan = 4096
+
 template <bool VEC4>
-__global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
+__global__ __launch_bounds__(256) void accept_partial_kernel(AcceptArgs a) {
   __shared__ float sv[4];
   __shared__ int si[4];
-  __shared__ int last;
-  __shared__ int t[256];
-  __shared__ int acc_len;
   const int row = blockIdx.y, part = blockIdx.x, tid = threadIdx.x;
   const int start = part * a.part_len;
   const int end = min(start + a.part_len, a.vocab);
   const float* L = a.logits + (int64_t)row * a.vocab;
   float bv = -INFINITY;
   int bi = INT_MAX;
+  // a part is at most kScan * 256 elements: every load of the scan is issued before the first
+  // compare (clamped to the part; duplicates of the last element cannot win, they only tie
+  // with a lower index of the same value)
   if (VEC4) {
-    // start and the row are 16-byte aligned (vocab and part_len are multiples of 4)
     const f32x4* L4 = reinterpret_cast<const f32x4*>(L);
-    for (int v = start + 4 * tid; v < end; v += 4 * 256) {
-      const f32x4 x = L4[v >> 2];
+    f32x4 x[kScan / 4];
+#pragma unroll
+    for (int u = 0; u < kScan / 4; ++u) {
+      const int v = min(start + 4 * tid + 1024 * u, end - 4);
+      x[u] = L4[v >> 2];
+    }
+#pragma unroll
+    for (int u = 0; u < kScan / 4; ++u) {
+      const int v = min(start + 4 * tid + 1024 * u, end - 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (better(x[e], v + e, bv, bi)) { bv = x[e]; bi = v + e; }
+        if (better(x[u][e], v + e, bv, bi)) { bv = x[u][e]; bi = v + e; }
     }
   } else {
-    for (int v = start + tid; v < end; v += 256) {
-      const float x = L[v];
-      if (better(x, v, bv, bi)) { bv = x; bi = v; }
+    float x[kScan];
+#pragma unroll
+    for (int u = 0; u < kScan; ++u) x[u] = L[min(start + tid + 256 * u, end - 1)];
+#pragma unroll
+    for (int u = 0; u < kScan; ++u) {
+      const int v = min(start + tid + 256 * u, end - 1);
+      if (better(x[u], v, bv, bi)) { bv = x[u]; bi = v; }
     }
   }
   wave_argmax(bv, bi);
@@ -65,40 +78,45 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
       if (better(sv[k], si[k], bv, bi)) { bv = sv[k]; bi = si[k]; }
     a.part_val[(int64_t)row * a.parts + part] = bv;
     a.part_idx[(int64_t)row * a.parts + part] = bi;
-    // release: this part is visible device-wide before the ticket is taken
-    __threadfence();
-    const unsigned total = (unsigned)(a.parts * a.n_rows);
-    last = atomicAdd(a.ticket, 1u) == total - 1;
   }
-  __syncthreads();
-  if (!last) return;
-  // acquire: every other workgroup's part is visible to this one
-  __threadfence();
+}
+
+__global__ __launch_bounds__(256) void accept_final_kernel(AcceptArgs a) {
+  __shared__ int t[256];
+  __shared__ int prop[256];
+  __shared__ int acc_len;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
   const int n_draft = a.n_rows - 1;
-  if (tid < a.n_rows) {
+  if (tid < n_draft) prop[tid] = a.proposals[tid];
+  // wave w reduces rows w, w+4, ...: lane p takes parts p, p+64, ... (one load round for up
+  // to 64 parts), then a shuffle reduction
+  for (int row2 = w; row2 < a.n_rows; row2 += 4) {
     float rv = -INFINITY;
     int ri = INT_MAX;
-    for (int p = 0; p < a.parts; ++p) {
-      const float v = __builtin_nontemporal_load(&a.part_val[(int64_t)tid * a.parts + p]);
-      const int i = __builtin_nontemporal_load(&a.part_idx[(int64_t)tid * a.parts + p]);
+    for (int p = tid & 63; p < a.parts; p += 64) {
+      const float v = a.part_val[(int64_t)row2 * a.parts + p];
+      const int i = a.part_idx[(int64_t)row2 * a.parts + p];
       if (better(v, i, rv, ri)) { rv = v; ri = i; }
     }
-    if (ri == INT_MAX) ri = 0;   // a row of NaNs only: any in-range index
-    t[tid] = ri;
-    if (a.row_argmax != nullptr) a.row_argmax[tid] = ri;
+    wave_argmax(rv, ri);
+    if ((tid & 63) == 0) {
+      if (ri == INT_MAX) ri = 0;   // a row of NaNs only: any in-range index
+      t[row2] = ri;
+      if (a.row_argmax != nullptr) a.row_argmax[row2] = ri;
+    }
   }
   __syncthreads();
   if (tid == 0) {
     int acc = n_draft;
     for (int r = 0; r < n_draft; ++r)
-      if (t[r] != a.proposals[r]) { acc = r; break; }
+      if (t[r] != prop[r]) { acc = r; break; }
     acc_len = acc;
     a.accept_len[0] = acc;
-    *a.ticket = 0u;             // ready for the next call
   }
   __syncthreads();
   const int acc = acc_len;
-  if (tid < a.n_rows) a.committed[tid] = tid < acc ? a.proposals[tid] : (tid == acc ? t[acc] : -1);
+  if (tid < a.n_rows) a.committed[tid] = tid < acc ? prop[tid] : (tid == acc ? t[acc] : -1);
 }
 
 }  // namespace
@@ -106,9 +124,12 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream) {
   const dim3 grid(a.parts, a.n_rows);
   if ((a.vocab & 3) == 0 && (a.part_len & 3) == 0)
-    hipLaunchKernelGGL(accept_kernel<true>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(accept_partial_kernel<true>, grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(accept_kernel<false>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(accept_partial_kernel<false>, grid, dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(accept_final_kernel, dim3(1), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

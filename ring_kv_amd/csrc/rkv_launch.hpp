@@ -29,8 +29,6 @@ struct ChunkAttnArgs {
   float* part_lse;        //                    and [Hkv][S][rows]
 };
 hipError_t launch_chunk_attn(const ChunkAttnArgs& a, hipStream_t stream);
-// One-launch window attention over a ring (no partials, no workspace); pt must be nullptr.
-hipError_t launch_ring_attn(const ChunkAttnArgs& a, hipStream_t stream);
 
 struct MergeArgs {
   const float* part_o;
@@ -72,7 +70,6 @@ struct AcceptArgs {
   int32_t* row_argmax;    // may be nullptr
   float* part_val;        // [n_rows][parts]
   int32_t* part_idx;      // [n_rows][parts]
-  uint32_t* ticket;       // zero on entry; the last workgroup resets it
   int32_t parts;
   int32_t part_len;
 };

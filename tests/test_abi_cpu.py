@@ -81,12 +81,12 @@ def test_ring_argument_checks():
     assert ring(window=0) == EARG
     assert ring(pos0=-1, head=0) == EARG
     assert ring(d=dims(dtype=0)) == EDTYPE
-    # the default one-launch path needs no workspace; an explicit split of the at most 10
-    # chunks that 527 positions touch needs [4][10][64][128] + [4][10][64] floats
-    assert L.verify_attn_ring_workspace_bytes(dims(), 2048, 512, 0) == 0
+    # 527 positions touch at most 10 chunks: one chunk per split by default, partials
+    # [4][10][64][128] + [4][10][64] floats
     want = 4 * 10 * 64 * 128 * 4 + 4 * 10 * 64 * 4
+    assert L.verify_attn_ring_workspace_bytes(dims(), 2048, 512, 0) == want
     assert L.verify_attn_ring_workspace_bytes(dims(), 2048, 512, 10) == want
-    assert ring(splits=10, ws=NULL) == EWS
+    assert ring(ws=NULL) == EWS
 
 
 def test_contiguous_and_merge_checks():
@@ -102,7 +102,7 @@ def test_contiguous_and_merge_checks():
 
 def test_accept_checks():
     need = L.verify_accept_workspace_bytes(16, 65536)
-    assert need == 2 * 1280 + 256     # 17 rows x 16 parts of 4096 logits, f32 + i32, + counter
+    assert need == 2 * 1280           # 17 rows x 16 parts of 4096 logits, f32 + i32, 256-B aligned
     assert L.verify_accept(NULL, 16, 65536, P, P, P, NULL, P, need, NULL) == ENULL
     assert L.verify_accept(P, 16, 65536, P, P, P, NULL, NULL, 0, NULL) == EWS
     assert L.verify_accept(P, 16, 65536, P, P, P, NULL, P, need - 1, NULL) == EWS
