@@ -16,9 +16,11 @@
 // of 16-key tiles the key order is permuted (sigma below) so that each lane's 8 P values
 // are 8 consecutive keys, which the dimension-major V chunk supplies as one 16-byte read.
 //
-// Memory path: K and V chunks are streamed from HBM with 16-byte loads (a wave reads 1 KiB
-// contiguous per instruction), two chunks ahead of the compute, staged in registers and
-// written into double-buffered, XOR-swizzled LDS tiles that all waves read.
+// Memory path: K and V chunks stream from HBM with 16-byte loads (a wave reads 1 KiB contiguous
+// per instruction) three chunks ahead of the compute, staged in registers and written into a
+// three-buffer ring of XOR-swizzled LDS tiles that all waves read.  (The direct HBM-to-LDS loads
+// of gfx950 were measured here at ~6 TB/s against ~7 TB/s for register loads of the same
+// blocks, so the data takes the register path.)
 #include "rkv_device.hpp"
 #include "rkv_launch.hpp"
 
@@ -74,54 +76,29 @@ struct Tile {
   }
 };
 
-// Direct HBM -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4): lane i of
-// the wave writes LDS bytes [lds_base + 16 i, +16).  Issued from inline assembly so that the
-// compiler neither reorders these loads nor inserts its own (all-draining) waits for them;
-// the kernel waits on the vector-memory counter itself.
-__device__ __forceinline__ void dma16(uint32_t lds_base, const void* gbase, uint32_t goff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(lds_base), "v"(goff), "s"(gbase) : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // Template parameters:
 //   NRG    row groups: wave (rg, kh) owns rows 16*rg .. 16*rg+15 of the KV head's rows
 //   KS     key halves: with KS = 2 each chunk's 64 keys are split between two waves per row
 //          group (keys 0..31 and 32..63); each keeps its own online-softmax state and the two
 //          states merge through LDS at the end.  Two waves per SIMD, each with half the
 //          dependent work per chunk.
-//   QLDS   Q comes in through the same direct-to-LDS path as K and V (rows <= 64), so no
-//          compiler-visible load precedes the chunk pipeline
 //   PAGED  slots come from the page table; otherwise the store is a ring (slot = c mod n_slots)
-template <int D, int NRG, int KS, bool QLDS, bool PAGED>
+template <int D, int NRG, int KS, bool PAGED>
 __global__ __launch_bounds__(NRG * KS * 64)
 void chunk_attn_kernel(ChunkAttnArgs a) {
   using T = Tile<D>;
   constexpr int NW = NRG * KS;
   constexpr int NT = NW * 64;
-  constexpr int NBUF = 4;
+  constexpr int NBUF = 3;                                // LDS tiles = register stages
   constexpr int LPC = (T::kPieces + T::vPieces) / NT;   // 16-byte loads per chunk per thread
   static_assert((T::kPieces + T::vPieces) % NT == 0, "pieces must divide evenly");
-  static_assert(T::kPieces % 64 == 0, "a wave's load must fall in one tile");
-  constexpr int PF = NBUF - 1;                           // chunks in flight ahead of compute
-  static_assert(PF * LPC < 64, "vmcnt range");
+  static_assert(T::kPieces % NT == 0, "a load index is all K or all V for every thread");
+  constexpr int PF = NBUF;                               // chunks in flight ahead of compute
   constexpr int KK = D / 32;
   constexpr int TMD = D / 16;
   constexpr int NKS = KS == 2 ? 1 : 2;                   // 32-key halves per wave per chunk
-  constexpr uint32_t kBufBytes = T::elems * 2;
-  constexpr int QP = QLDS ? 64 * D / 8 : 0;              // Q pieces (64 rows)
-  static_assert(!QLDS || NRG * 16 <= 64, "LDS Q holds 64 rows (one row tile)");
-  static_assert(QP % NT == 0, "Q pieces must divide evenly");
-  constexpr int QPT = QP / NT;
-  static_assert(PF * LPC + QPT < 64, "vmcnt range");
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[NBUF][T::elems];
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[QLDS ? 64 * D : 8];
   __shared__ int pt_lds[kPtCap];
 
   const int tid = threadIdx.x;
@@ -157,34 +134,21 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
 
   // Q^T operand of S^T = K Q^T: lane (ln, lq) holds row ln's dims kk*32 + 8*lq .. +7
   bf16x8 qop[KK];
-  if constexpr (!QLDS) {
+  auto load_q = [&]() __attribute__((always_inline)) {
     const uint16_t* qrow = a.q + ((int64_t)qi * a.n_q_heads + hq) * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      u32x4 raw = {0u, 0u, 0u, 0u};
-      if (row_ok) raw = *reinterpret_cast<const u32x4*>(qrow + kk * 32 + lq * 8);
+      // qi, hq are clamped to row 0 for rows past the end: load, then zero
+      u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + kk * 32 + lq * 8);
+      if (!row_ok) raw = u32x4{0u, 0u, 0u, 0u};
       qop[kk] = __builtin_bit_cast(bf16x8, raw);
     }
-  }
+  };
 
-  // ---- page-table slice in LDS: entry for local chunk loc at pt_lds[loc % kPtCap] -----
-  // Filled once for the first kPtCap chunks; splits longer than that refresh one half of the
-  // slice at a time, 128 chunks before it is needed.
   constexpr bool paged = PAGED;
-  if (paged) {
-    for (int e = tid; e < kPtCap && e < nloc; e += NT) pt_lds[e] = a.pt[c_lo + e];
-  }
-  // Register Q and the table slice are complete before any direct-to-LDS load is issued, so
-  // the compiler's own waits for them never cover one of those loads.
-  if constexpr (!QLDS) {
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(qop[kk]));
-  }
-  lds_barrier();
-
   // ring: slot = logical chunk mod n_slots; a ring span covers at most n_slots + 1 chunks
   const int ring_base = paged ? 0 : (int)(c_lo % a.n_slots);
-  auto slot_of = [&](int loc) -> int {
+  auto slot_of = [&](int loc) __attribute__((always_inline)) -> int {
     if (!paged) {
       int t = ring_base + loc;
       t -= t >= a.n_slots ? a.n_slots : 0;
@@ -193,7 +157,7 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
     }
     return __builtin_amdgcn_readfirstlane(pt_lds[loc & (kPtCap - 1)]);
   };
-  auto maybe_refresh_table = [&](int loc) {
+  auto maybe_refresh_table = [&](int loc) __attribute__((always_inline)) {
     // at loc = 256k + 128 (k >= 1) load local chunks [256(k+1), 256(k+2)) into half (k+1)&1,
     // which last held chunks [256(k-1), 256k), all issued by now
     if (!paged || nloc <= kPtCap || (loc & 255) != 128 || loc < 256) return;
@@ -203,31 +167,54 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
       if (base + e < nloc) pt_lds[(base + e) & (kPtCap - 1)] = a.pt[c_lo + base + e];
   };
 
-  const uint32_t lds_base = (uint32_t)(uintptr_t)&lds[0][0];
-  // Chunk loc -> LDS buffer loc % NBUF.  LDS piece P of a buffer (P = u*NT + 64w + lane) holds
-  // global piece P with the XOR swizzle undone, so every wave instruction still reads 1 KiB of
-  // contiguous HBM.  An out-of-range slot loads slot 0 instead (the chunk is skipped in compute)
-  // so that every thread always has exactly LPC loads per chunk outstanding.
-  auto issue = [&](int loc) {
-    int slot = slot_of(loc);
-    if ((unsigned)slot >= (unsigned)a.n_slots) slot = 0;
+  // Register stages: chunk loc is loaded into stage loc % 3 (piece P = u*NT + tid of the chunk,
+  // so each wave instruction reads 1 KiB of contiguous HBM) and written to LDS tile loc % 3 at
+  // its swizzled place.  A chunk past the split, or with an out-of-range slot, loads one line of
+  // slot 0 instead (cached, never computed), so every iteration has the same loads in flight and
+  // the compiler's wait counts stay exact.
+  u32x4 stg0[LPC], stg1[LPC], stg2[LPC];
+  auto stage = [&](auto st_tag) __attribute__((always_inline)) -> u32x4* {
+    constexpr int S = decltype(st_tag)::value;
+    if constexpr (S == 0) return stg0;
+    else if constexpr (S == 1) return stg1;
+    else return stg2;
+  };
+  // Branch-free on purpose: the slot, the base and a lane-offset mask are uniform selects, so
+  // every step issues the same loads and the wait counts before each commit stay exact.
+  // cand: the chunk's slot as the table or ring gives it (garbage past the split: masked)
+  auto issue = [&](auto st_tag, int loc, int cand) __attribute__((always_inline)) {
+    u32x4* st = stage(st_tag);
+    const bool ok = loc < nloc && (unsigned)cand < (unsigned)a.n_slots;
+    const int slot = ok ? cand : 0;
+    const uint32_t keep = ok ? 0xffffffffu : 0u;        // 0: every lane reads piece 0
     const int64_t blk = (int64_t)slot * a.n_kv_heads + g;
     const uint16_t* kb = a.k + blk * (64 * D);
     const uint16_t* vb = a.v + blk * (64 * D);
-    const uint32_t lb = lds_base + (uint32_t)(loc % NBUF) * kBufBytes;
 #pragma unroll
     for (int u = 0; u < LPC; ++u) {
-      const int pw = u * NT + w * 64;                     // first piece of this wave's load
-      const int P = pw + lane;
-      const uint32_t m0 = __builtin_amdgcn_readfirstlane(lb + (uint32_t)pw * 16u);
-      if (pw < T::kPieces) {
-        const int key = P / T::kRow, phys = P % T::kRow;
-        dma16(m0, kb, (uint32_t)(key * T::kRow + (phys ^ swz_k<D>(key))) * 16u);
+      const int P = u * NT + tid;
+      const uint16_t* src = (u * NT < T::kPieces)
+                                ? kb + (((uint32_t)P * 8u) & keep)
+                                : vb + (((uint32_t)(P - T::kPieces) * 8u) & keep);
+      st[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+    }
+  };
+  auto commit = [&](auto st_tag) __attribute__((always_inline)) {
+    constexpr int S = decltype(st_tag)::value;
+    const u32x4* st = stage(st_tag);
+    uint16_t* buf = &lds[S][0];
+#pragma unroll
+    for (int u = 0; u < LPC; ++u) {
+      const int P = u * NT + tid;
+      int off;
+      if (u * NT < T::kPieces) {
+        const int key = P / T::kRow, pc = P % T::kRow;
+        off = T::k_off(key, pc);
       } else {
         const int vp = P - T::kPieces;
-        const int d = vp >> 3, phys = vp & 7;
-        dma16(m0, vb, (uint32_t)(d * 8 + (phys ^ swz_v(d))) * 16u);
+        off = T::v_off(vp >> 3, vp & 7);
       }
+      *reinterpret_cast<u32x4*>(buf + off) = st[u];
     }
   };
 
@@ -248,7 +235,7 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
 
   // EDGE: some key of the chunk is invisible to some row (causal tail, window start) or lies
   // outside the stored range; interior chunks run without any masking code.
-  auto compute_body = [&](const uint16_t* buf, int64_t cbase, bool partial, auto edge_tag) {
+  auto compute_body = [&](const uint16_t* buf, int64_t cbase, bool partial, auto edge_tag) __attribute__((always_inline)) {
     constexpr bool EDGE = decltype(edge_tag)::value;
     f32x4 sacc[2 * NKS];
 #pragma unroll
@@ -342,9 +329,9 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
     }
   };
 
-  auto compute = [&](const uint16_t* buf, int loc) {
-    if (!wave_active) return;
-    if ((unsigned)slot_of(loc) >= (unsigned)a.n_slots) return;   // no slot: adds nothing
+  auto compute = [&](const uint16_t* buf, int loc, int slot) __attribute__((always_inline)) {
+    if (!wave_active || loc >= nloc) return;
+    if ((unsigned)slot >= (unsigned)a.n_slots) return;   // no slot: adds nothing
     const int64_t cbase = (c_lo + loc) * 64;
     const bool partial = cbase < a.valid_lo || cbase + 64 > a.valid_hi;
     const bool edge = (cbase + 63 > p_first) || (cbase < lo_last) || partial;
@@ -354,51 +341,60 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
       compute_body(buf, cbase, partial, std::false_type{});
   };
 
-  // ---- pipeline: Q, then PF chunks in flight while one is computed ---------------------
-  if constexpr (QLDS) {
-    if (nloc > 0) {
-      // Q rows of this KV head, row r = i*G + (h - g*G) at LDS row r; rows past the last are
-      // loaded from row 0 (any valid address) and never written out
-      const uint32_t qb = (uint32_t)(uintptr_t)&q_lds[0];
-#pragma unroll
-      for (int u = 0; u < QPT; ++u) {
-        const int pw = u * NT + w * 64;
-        const int P = pw + lane;
-        const int rr = P / (D / 8), pc = P % (D / 8);
-        const int rs = rr < rows ? rr : 0;
-        const int64_t qoff = (((int64_t)(rs / G) * a.n_q_heads + g * G + rs % G) * D + pc * 8) * 2;
-        dma16(__builtin_amdgcn_readfirstlane(qb + (uint32_t)pw * 16u), a.q, (uint32_t)qoff);
-      }
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < PF; ++k)
-    if (k < nloc) issue(k);
-  if constexpr (QLDS) {
-    if (nloc > 0) {
-      // wait for Q alone (the chunks issued after it stay in flight)
-      const int after = nloc < PF ? nloc : PF;
-      if (after >= 3) wait_vmcnt<3 * LPC>();
-      else if (after == 2) wait_vmcnt<2 * LPC>();
-      else wait_vmcnt<LPC>();
-      lds_barrier();
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        qop[kk] = *reinterpret_cast<const bf16x8*>(&q_lds[r * D + kk * 32 + lq * 8]);
-    }
-  }
-
-  for (int loc = 0; loc < nloc; ++loc) {
-    // chunks issued after this one: min(PF-1, nloc-1-loc); wait until only they are in flight
-    const int ahead = nloc - 1 - loc;
-    if (ahead >= PF - 1) wait_vmcnt<(PF - 1) * LPC>();
-    else if (PF >= 3 && ahead == 1) wait_vmcnt<LPC>();
-    else wait_vmcnt<0>();
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  if (nloc <= 1) {
+    // ---- one chunk (the ring's default split): its loads and Q's go out together -------
+    const int cand = paged ? (nloc == 1 ? __builtin_amdgcn_readfirstlane(a.pt[c_lo]) : -1)
+                           : ring_base;
+    issue(I0{}, 0, cand);
+    load_q();
+    commit(I0{});
     lds_barrier();
-    // refill the buffer computed in the previous step (every wave is past it now)
-    maybe_refresh_table(loc + PF);
-    if (loc + PF < nloc) issue(loc + PF);
-    compute(&lds[loc % NBUF][0], loc);
+    compute(&lds[0][0], 0, cand);
+  } else {
+    load_q();
+    // ---- page-table slice in LDS: entry for local chunk loc at pt_lds[loc % kPtCap] ---
+    // Filled once for the first kPtCap chunks; splits longer than that refresh one half of
+    // the slice at a time, 128 chunks before it is needed.
+    if (paged) {
+      for (int e = tid; e < kPtCap && e < nloc; e += NT) pt_lds[e] = a.pt[c_lo + e];
+    }
+    // Q and the table slice are complete before the first chunk load is issued: left
+    // pending, the wait-count analysis would merge them into the chunk loop and drain it at
+    // every use.
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(qop[kk]));
+    lds_barrier();
+
+    // ---- pipeline: three chunks in flight in registers while one is computed ------------
+    // Step loc: write chunk loc from its register stage into LDS tile loc % 3, refill that
+    // stage with chunk loc + 3, barrier, compute chunk loc.  Tile loc % 3 was last read by the
+    // compute of chunk loc - 3, which every wave finished before the barrier of step loc - 2.
+    // The scheduler may not reorder the first three issues: stage 0 must be the oldest loads.
+    issue(I0{}, 0, slot_of(0));
+    __builtin_amdgcn_sched_barrier(0);
+    issue(I1{}, 1, slot_of(1));
+    __builtin_amdgcn_sched_barrier(0);
+    issue(I2{}, 2, slot_of(2));
+    __builtin_amdgcn_sched_barrier(0);
+    auto step = [&](auto st_tag, int loc) __attribute__((always_inline)) {
+      constexpr int S = decltype(st_tag)::value;
+      commit(st_tag);
+      maybe_refresh_table(loc + PF);
+      issue(st_tag, loc + PF, slot_of(loc + PF));
+      lds_barrier();
+      compute(&lds[S][0], loc, slot_of(loc));
+    };
+    // All three steps run unconditionally (a step past the split computes nothing): with a
+    // conditional step the skipped path would have fewer loads in flight, and the wait counts
+    // at the join would be set for that path.
+    for (int loc = 0; loc < nloc; loc += NBUF) {
+      step(I0{}, loc);
+      step(I1{}, loc + 1);
+      step(I2{}, loc + 2);
+    }
   }
 
   // ---- epilogue ------------------------------------------------------------------------
@@ -456,25 +452,24 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
   }
 }
 
-template <int D, int NRG, int KS, bool QLDS>
+template <int D, int NRG, int KS>
 hipError_t launch_t(const ChunkAttnArgs& a, hipStream_t stream) {
   const int rows = a.q_len * a.G;
   const dim3 blocks(a.n_kv_heads * a.num_splits, (rows + NRG * 16 - 1) / (NRG * 16));
   const dim3 threads(NRG * KS * 64);
   if (a.pt != nullptr)
-    hipLaunchKernelGGL((chunk_attn_kernel<D, NRG, KS, QLDS, true>), blocks, threads, 0, stream, a);
+    hipLaunchKernelGGL((chunk_attn_kernel<D, NRG, KS, true>), blocks, threads, 0, stream, a);
   else
-    hipLaunchKernelGGL((chunk_attn_kernel<D, NRG, KS, QLDS, false>), blocks, threads, 0, stream, a);
+    hipLaunchKernelGGL((chunk_attn_kernel<D, NRG, KS, false>), blocks, threads, 0, stream, a);
   return hipGetLastError();
 }
 
+// Tiles of 64 rows (blockIdx.y), two waves per row group (key halves).  Tiles of one split
+// each read its chunks; a variant with more row groups per workgroup would need more registers
+// than the three register stages leave.
 template <int D>
 hipError_t launch_d(const ChunkAttnArgs& a, hipStream_t stream) {
-  const int rows = a.q_len * a.G;
-  // up to 64 rows: one row tile, two waves per row group (key halves), Q through LDS;
-  // more rows: tiles of 128 rows (blockIdx.y), eight waves without key split
-  if (rows <= 64) return launch_t<D, 4, 2, true>(a, stream);
-  return launch_t<D, 8, 1, false>(a, stream);
+  return launch_t<D, 4, 2>(a, stream);
 }
 
 }  // namespace
