@@ -14,6 +14,10 @@ over a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload stack_40l_131k|paged_256k]
     python bench.py --mode copy     # plain 1-GiB device copies, for HBM counter calibration
+    python bench.py --mode kernel   # the dominant kernel alone (10 launches), for counter runs
+    python bench.py --mode traffic --fetch F.csv --write W.csv --copy-fetch CF.csv --copy-write CW.csv
+                                    # HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE /
+                                    # WRITE_SIZE counter files, scaled by the copy calibration
 """
 from __future__ import annotations
 
@@ -44,7 +48,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="stack_40l_131k",
                     choices=["stack_40l_131k", "paged_256k"])
-    ap.add_argument("--mode", default="bench", choices=["bench", "copy"])
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy", "kernel", "traffic"])
+    for f in ("fetch", "write", "copy_fetch", "copy_write"):
+        ap.add_argument("--" + f.replace("_", "-"), default=None)
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-256k", action="store_true", help="skip the 262,144-context layer")
@@ -53,6 +59,23 @@ def parse():
 
 def kernel_hash() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def graph_ms(fn, inner, reps, torch):
+    """ms per call of fn: `inner` calls captured in one HIP graph, replayed `reps` times."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(inner):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    return event_ms(g.replay, reps, torch) / inner
 
 
 def event_ms(fn, n, torch):
@@ -151,6 +174,56 @@ def cpu_baseline(synth, oracle):
                       "40-layer step; KV bytes of the sample / wall time"}
 
 
+def counter_kib(path, kernel_substr):
+    """Mean Counter_Value (KiB per dispatch) over the dispatches of one kernel in a rocprofv3
+    counter_collection.csv."""
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+            if kernel_substr in r["Kernel_Name"]]
+    if not vals:
+        raise SystemExit(f"{path}: no dispatch of a kernel named like {kernel_substr!r}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def traffic_summary(args):
+    """HBM bytes per launch of the paged split kernel at 131,072: FETCH_SIZE and WRITE_SIZE (KiB
+    per dispatch), each scaled by the bytes a plain 1-GiB device copy moves over what the same
+    counter reads for it."""
+    copy_bytes = 1 << 30
+    cf, _ = counter_kib(args.copy_fetch, "copy")
+    cw, _ = counter_kib(args.copy_write, "copy")
+    kf, n = counter_kib(args.fetch, "chunk_attn_kernel")
+    kw, _ = counter_kib(args.write, "chunk_attn_kernel")
+    f_scale, w_scale = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    fetch, write = kf * 1024 * f_scale, kw * 1024 * w_scale
+    algo = 2 * 131072 * 4 * 128 * 2
+    out = {"kernel": "chunk_attn_kernel (paged, split-K, 64 splits) at 131,072",
+           "kernel_sha": kernel_hash(), "dispatches": n,
+           "fetch_kib_raw": kf, "write_kib_raw": kw,
+           "copy_fetch_kib_raw": cf, "copy_write_kib_raw": cw,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "hbm_fetch_bytes_per_launch": round(fetch), "hbm_write_bytes_per_launch": round(write),
+           "hbm_bytes_per_launch": round(fetch + write),
+           "algorithmic_bytes_per_launch": algo,
+           "traffic_over_algorithmic": round((fetch + write) / algo, 4),
+           "commands": [
+               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_k_FETCH_SIZE -o p "
+               "-- python3 bench.py --mode kernel",
+               "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_k_WRITE_SIZE -o p "
+               "-- python3 bench.py --mode kernel",
+               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_c_FETCH_SIZE -o p "
+               "-- python3 bench.py --mode copy",
+               "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_c_WRITE_SIZE -o p "
+               "-- python3 bench.py --mode copy",
+               "python3 bench.py --mode traffic --fetch gpurun_out/pmc_k_FETCH_SIZE/p_counter_collection.csv "
+               "--write gpurun_out/pmc_k_WRITE_SIZE/p_counter_collection.csv "
+               "--copy-fetch gpurun_out/pmc_c_FETCH_SIZE/p_counter_collection.csv "
+               "--copy-write gpurun_out/pmc_c_WRITE_SIZE/p_counter_collection.csv"]}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out), flush=True)
+
+
 def traffic_entry(per_launch_bytes):
     if not os.path.exists(TRAFFIC_FILE):
         return None
@@ -169,6 +242,9 @@ def main():
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
+    if args.mode == "traffic":
+        traffic_summary(args)
+        return
     import torch
 
     if not torch.cuda.is_available():
@@ -189,7 +265,24 @@ def main():
                           "gbps": 2 * n / ms / 1e6}), flush=True)
         return
 
+    import ctypes
+
     import synth
+    from ring_kv_amd._lib import AttnDims
+
+    if args.mode == "kernel":
+        # the dominant kernel alone: 10 launches of the paged split kernel over one layer
+        c, _ = synth.workload("stack_40l_131k", 3, keep_rows=False)
+        t = lambda a: rk.tensor_from_numpy(a, "cuda")  # noqa: E731
+        q, kp, vp, pt = t(c.q), t(c.k_pool), t(c.v_pool), t(c.page_table)
+        splits = rk.verify_attn_paged_auto_splits(16, 4, 128, 16, 131072)
+        po = torch.empty((4, splits, 64, 128), dtype=torch.float32, device="cuda")
+        pl = torch.empty((4, splits, 64), dtype=torch.float32, device="cuda")
+        for _ in range(10):
+            rk.verify_attn_paged_partial(q, kp, vp, pt, 131072, splits, part_out=po, part_lse=pl)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "kernel", "launches": 10, "splits": splits}), flush=True)
+        return
 
     res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
@@ -222,11 +315,10 @@ def main():
             ms = event_ms(g.replay, args.steps, torch)
             graph = True
             log(f"graph step {ms:.3f} ms")
-        # dominant kernel: paged split-K at 131,072, 10 launches per round
-        for _ in range(2):
-            st.paged_partial_round()
-        rounds = max(2, args.steps // 4)
-        k_ms = event_ms(st.paged_partial_round, rounds, torch) / 10
+        # dominant kernel: the paged split-K kernel at 131,072 over the 10 paged layers, one
+        # round of 10 launches captured in a HIP graph; HIP events on the replay stream
+        st.paged_partial_round()
+        k_ms = graph_ms(st.paged_partial_round, 2, max(3, args.steps // 2), torch) / 10
         per_launch = 2 * 131072 * 4 * 128 * 2
         achieved = per_launch / (k_ms * 1e-3) / 1e9
         log(f"paged split kernel {k_ms * 1e3:.1f} us/launch, {achieved:.0f} GB/s")
@@ -261,14 +353,19 @@ def main():
         splits = rk.verify_attn_paged_auto_splits(16, 4, 128, 16, 262144)
         po = torch.empty((4, splits, 64, 128), dtype=torch.float32, device="cuda")
         pl = torch.empty((4, splits, 64), dtype=torch.float32, device="cuda")
-        fn = lambda: rk.verify_attn_paged(q, kp, vp, pt, 262144, out=out, lse=lse)  # noqa: E731
+        ws = torch.empty(rk.lib().verify_attn_paged_workspace_bytes(
+            ctypes.byref(AttnDims(16, 16, 4, 128, 0.0, 1)), 262144, 64, 0), dtype=torch.uint8,
+            device="cuda")
+        fn = lambda: rk.verify_attn_paged(q, kp, vp, pt, 262144, out=out, lse=lse,  # noqa: E731
+                                          workspace=ws)
         part = lambda: rk.verify_attn_paged_partial(q, kp, vp, pt, 262144, splits,  # noqa: E731
                                                     part_out=po, part_lse=pl)
         for _ in range(max(2, args.warmup)):
             fn()
         n = max(5, args.steps)
-        us = event_ms(fn, n, torch) * 1e3
-        us_split = event_ms(part, n, torch) * 1e3
+        # graph replay, as in the step: n layers per graph, HIP events around the replays
+        us = graph_ms(fn, n, 3, torch) * 1e3
+        us_split = graph_ms(part, n, 3, torch) * 1e3
         log(f"256K layer {us:.1f} us (split kernel {us_split:.1f} us)")
         res.update({"us_per_layer_256k": round(us, 2),
                     "kv_gbps_256k": round(kv / (us * 1e-6) / 1e9, 1),

@@ -59,6 +59,13 @@ __device__ __forceinline__ float row_max4(float v) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// Positions inside a workgroup are 32-bit offsets from its split's first key, clamped to
+// +-2^29 (a split spans at most kMaxSplitChunks chunks, 2^28 positions), so every edge test is a
+// 32-bit scalar or vector compare.
+__device__ __forceinline__ int rel_pos(int64_t x, int64_t base) {
+  return (int)imax64(-(int64_t(1) << 29), imin64(x - base, int64_t(1) << 29));
+}
+
 constexpr int kPtCap = 512;   // page-table entries kept in LDS (a power of two, >= 512)
 
 template <int D>
@@ -89,17 +96,23 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
   using T = Tile<D>;
   constexpr int NW = NRG * KS;
   constexpr int NT = NW * 64;
-  constexpr int NBUF = 3;                                // LDS tiles = register stages
+  // Chunks in flight = register stages NST; chunk loc goes through stage loc % NST and LDS
+  // tile loc % NLDS.  Two tiles suffice: the barrier of step loc - 1 follows every wave's
+  // compute of chunk loc - 2, the last reader of the tile that step loc overwrites.
+  constexpr int NST = 2;
+  constexpr int NLDS = 2;
+  static_assert(NST % NLDS == 0 && NST >= 2 && NST <= 4, "stage / tile counts");
   constexpr int LPC = (T::kPieces + T::vPieces) / NT;   // 16-byte loads per chunk per thread
   static_assert((T::kPieces + T::vPieces) % NT == 0, "pieces must divide evenly");
   static_assert(T::kPieces % NT == 0, "a load index is all K or all V for every thread");
-  constexpr int PF = NBUF;                               // chunks in flight ahead of compute
+  constexpr int PF = NST;                                // chunks in flight ahead of compute
   constexpr int KK = D / 32;
   constexpr int TMD = D / 16;
   constexpr int NKS = KS == 2 ? 1 : 2;                   // 32-key halves per wave per chunk
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds[NBUF][T::elems];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[NLDS][T::elems];
   __shared__ int pt_lds[kPtCap];
+  __shared__ int wave_flag[NW];   // per wave: a table entry of the split is out of range
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -125,12 +138,17 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
   const bool row_ok = r < rows;
   const int qi = row_ok ? r / G : 0;
   const int hq = g * G + (row_ok ? r % G : 0);
-  const int64_t p_i = a.p0 + qi;
-  const int64_t lo_i = a.window > 0 ? imax64(0, p_i - a.window + 1) : 0;
   const bool wave_active = row0 + rg * 16 < rows;
-  const int64_t p_first = a.p0;
+  // key position bounds, relative to this split's first key c_lo * 64
+  const int64_t pbase = c_lo * 64;
+  const int64_t p_i64 = a.p0 + qi;
+  const int p_i = rel_pos(p_i64, pbase);                             // this row's query
+  const int lo_i = rel_pos(a.window > 0 ? imax64(0, p_i64 - a.window + 1) : 0, pbase);
+  const int p_first = rel_pos(a.p0, pbase);                          // first query of the block
   const int64_t p_last = a.p0 + a.q_len - 1;
-  const int64_t lo_last = a.window > 0 ? imax64(0, p_last - a.window + 1) : 0;
+  const int lo_last = rel_pos(a.window > 0 ? imax64(0, p_last - a.window + 1) : 0, pbase);
+  const int vlo = rel_pos(a.valid_lo, pbase);                        // stored keys [vlo, vhi)
+  const int vhi = rel_pos(a.valid_hi, pbase);
 
   // Q^T operand of S^T = K Q^T: lane (ln, lq) holds row ln's dims kk*32 + 8*lq .. +7
   bf16x8 qop[KK];
@@ -157,9 +175,10 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
     }
     return __builtin_amdgcn_readfirstlane(pt_lds[loc & (kPtCap - 1)]);
   };
-  auto maybe_refresh_table = [&](int loc) __attribute__((always_inline)) {
+  auto maybe_refresh_table = [&](int loc, auto refresh_tag) __attribute__((always_inline)) {
     // at loc = 256k + 128 (k >= 1) load local chunks [256(k+1), 256(k+2)) into half (k+1)&1,
     // which last held chunks [256(k-1), 256k), all issued by now
+    if constexpr (!decltype(refresh_tag)::value) return;
     if (!paged || nloc <= kPtCap || (loc & 255) != 128 || loc < 256) return;
     const int base = ((loc >> 8) + 1) << 8;
     if (base >= nloc) return;
@@ -167,17 +186,26 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
       if (base + e < nloc) pt_lds[(base + e) & (kPtCap - 1)] = a.pt[c_lo + base + e];
   };
 
-  // Register stages: chunk loc is loaded into stage loc % 3 (piece P = u*NT + tid of the chunk,
-  // so each wave instruction reads 1 KiB of contiguous HBM) and written to LDS tile loc % 3 at
-  // its swizzled place.  A chunk past the split, or with an out-of-range slot, loads one line of
+  // Register stages: chunk loc is loaded into stage loc % NST (piece P = u*NT + tid of the chunk,
+  // so each wave instruction reads 1 KiB of contiguous HBM) and written to LDS tile loc % NLDS
+  // at its swizzled place.  A chunk past the split, or with an out-of-range slot, loads one line of
   // slot 0 instead (cached, never computed), so every iteration has the same loads in flight and
   // the compiler's wait counts stay exact.
-  u32x4 stg0[LPC], stg1[LPC], stg2[LPC];
+  u32x4 stg0[LPC], stg1[LPC], stg2[LPC], stg3[LPC];
+  int sl0 = -1, sl1 = -1, sl2 = -1, sl3 = -1;   // slot of each stage's chunk (-1: none), uniform
   auto stage = [&](auto st_tag) __attribute__((always_inline)) -> u32x4* {
     constexpr int S = decltype(st_tag)::value;
     if constexpr (S == 0) return stg0;
     else if constexpr (S == 1) return stg1;
-    else return stg2;
+    else if constexpr (S == 2) return stg2;
+    else return stg3;
+  };
+  auto stage_slot = [&](auto st_tag) __attribute__((always_inline)) -> int& {
+    constexpr int S = decltype(st_tag)::value;
+    if constexpr (S == 0) return sl0;
+    else if constexpr (S == 1) return sl1;
+    else if constexpr (S == 2) return sl2;
+    else return sl3;
   };
   // Branch-free on purpose: the slot, the base and a lane-offset mask are uniform selects, so
   // every step issues the same loads and the wait counts before each commit stay exact.
@@ -186,6 +214,7 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
     u32x4* st = stage(st_tag);
     const bool ok = loc < nloc && (unsigned)cand < (unsigned)a.n_slots;
     const int slot = ok ? cand : 0;
+    stage_slot(st_tag) = ok ? cand : -1;
     const uint32_t keep = ok ? 0xffffffffu : 0u;        // 0: every lane reads piece 0
     const int64_t blk = (int64_t)slot * a.n_kv_heads + g;
     const uint16_t* kb = a.k + blk * (64 * D);
@@ -202,7 +231,7 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
   auto commit = [&](auto st_tag) __attribute__((always_inline)) {
     constexpr int S = decltype(st_tag)::value;
     const u32x4* st = stage(st_tag);
-    uint16_t* buf = &lds[S][0];
+    uint16_t* buf = &lds[S % NLDS][0];
 #pragma unroll
     for (int u = 0; u < LPC; ++u) {
       const int P = u * NT + tid;
@@ -233,9 +262,10 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
                       : u32x4{0u, 0u, 0u, 0u});
   const float csc = a.scale_log2;
 
-  // EDGE: some key of the chunk is invisible to some row (causal tail, window start) or lies
-  // outside the stored range; interior chunks run without any masking code.
-  auto compute_body = [&](const uint16_t* buf, int64_t cbase, bool partial, auto edge_tag) __attribute__((always_inline)) {
+  // EDGE: some key of the chunk may be invisible to some row (causal tail, window start), lie
+  // outside the stored range (partial) or come from no slot (ok false: the stage holds filler);
+  // interior chunks run without any masking code.
+  auto compute_body = [&](const uint16_t* buf, int cbase, bool partial, bool ok, auto edge_tag) __attribute__((always_inline)) {
     constexpr bool EDGE = decltype(edge_tag)::value;
     f32x4 sacc[2 * NKS];
 #pragma unroll
@@ -254,11 +284,9 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
     // key index within the chunk of score (j, i): 32*ks + 8*lq + 4*(j&1) + i
     float mx = -INFINITY;
     if constexpr (EDGE) {
-      // visible keys of this row: [vis_lo, vis_hi] relative to the chunk, clamped to 32 bits
-      const int64_t lo = imax64(lo_i, a.valid_lo) - cbase;
-      const int64_t hi = imin64(p_i, a.valid_hi - 1) - cbase;
-      const int vis_lo = (int)imax64(-1, imin64(lo, 64));
-      const int vis_hi = row_ok ? (int)imax64(-1, imin64(hi, 64)) : -1;
+      // visible keys of this row: [vis_lo, vis_hi] relative to the chunk
+      const int vis_lo = max(-1, min(max(lo_i, vlo) - cbase, 64));
+      const int vis_hi = (row_ok && ok) ? max(-1, min(min(p_i, vhi - 1) - cbase, 64)) : -1;
 #pragma unroll
       for (int j = 0; j < 2 * NKS; ++j) {
         const int ks = KS == 2 ? kh : (j >> 1);
@@ -308,12 +336,13 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
       const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pw[h][0], pw[h][1], pw[h][2], pw[h][3]});
       uint32_t vmask[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
       if constexpr (EDGE) {
-        // keys outside the stored range: zero their V so that 0 * (anything) stays 0
-        if (partial) {
+        // keys outside the stored range or without a slot: zero their V so that
+        // 0 * (anything) stays 0
+        if (partial || !ok) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const int64_t jj = cbase + 32 * ks + 8 * lq + e;
-            if (jj < a.valid_lo || jj >= a.valid_hi) vmask[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+            const int jj = cbase + 32 * ks + 8 * lq + e;
+            if (!ok || jj < vlo || jj >= vhi) vmask[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
           }
         }
       }
@@ -329,21 +358,29 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
     }
   };
 
-  auto compute = [&](const uint16_t* buf, int loc, int slot) __attribute__((always_inline)) {
-    if (!wave_active || loc >= nloc) return;
-    if ((unsigned)slot >= (unsigned)a.n_slots) return;   // no slot: adds nothing
-    const int64_t cbase = (c_lo + loc) * 64;
-    const bool partial = cbase < a.valid_lo || cbase + 64 > a.valid_hi;
-    const bool edge = (cbase + 63 > p_first) || (cbase < lo_last) || partial;
-    if (edge)
-      compute_body(buf, cbase, partial, std::true_type{});
-    else
-      compute_body(buf, cbase, partial, std::false_type{});
+  // Every wave computes every chunk it is given, even a wave whose rows are all past the end
+  // (its Q is zero and nothing of it is written): a skip would be a control-flow join at which
+  // the compiler copies all accumulators.
+  auto compute = [&](const uint16_t* buf, int loc, int slot, auto edge_tag) __attribute__((always_inline)) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
+    const int cbase = loc * 64;
+    if constexpr (EDGE) {
+      const bool partial = cbase < vlo || cbase + 64 > vhi;
+      compute_body(buf, cbase, partial, (unsigned)slot < (unsigned)a.n_slots, std::true_type{});
+    } else {
+      compute_body(buf, cbase, false, true, std::false_type{});
+    }
   };
+
+  // A one-chunk split takes the masking path when its chunk meets the window start, the causal
+  // tail or an end of the stored range.
+  const bool span_edge = nloc > 0 && ((nloc - 1) * 64 + 63 > p_first || lo_last > 0 ||
+                                      vlo > 0 || nloc * 64 > vhi);
 
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
   if (nloc <= 1) {
     // ---- one chunk (the ring's default split): its loads and Q's go out together -------
     const int cand = paged ? (nloc == 1 ? __builtin_amdgcn_readfirstlane(a.pt[c_lo]) : -1)
@@ -352,14 +389,26 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
     load_q();
     commit(I0{});
     lds_barrier();
-    compute(&lds[0][0], 0, cand);
+    if (nloc == 1) {
+      if (span_edge || (unsigned)cand >= (unsigned)a.n_slots)
+        compute(&lds[0][0], 0, cand, std::true_type{});
+      else
+        compute(&lds[0][0], 0, cand, std::false_type{});
+    }
   } else {
     load_q();
     // ---- page-table slice in LDS: entry for local chunk loc at pt_lds[loc % kPtCap] ---
     // Filled once for the first kPtCap chunks; splits longer than that refresh one half of
-    // the slice at a time, 128 chunks before it is needed.
+    // the slice at a time, 128 chunks before it is needed (and always take the masking path,
+    // as their later entries are not checked here).
+    bool bad = false;
     if (paged) {
-      for (int e = tid; e < kPtCap && e < nloc; e += NT) pt_lds[e] = a.pt[c_lo + e];
+      for (int e = tid; e < kPtCap && e < nloc; e += NT) {
+        const int sl = a.pt[c_lo + e];
+        pt_lds[e] = sl;
+        bad |= (unsigned)sl >= (unsigned)a.n_slots;
+      }
+      if (lane == 0) wave_flag[w] = __builtin_amdgcn_ballot_w64(bad) != 0;
     }
     // Q and the table slice are complete before the first chunk load is issued: left
     // pending, the wait-count analysis would merge them into the chunk loop and drain it at
@@ -367,33 +416,77 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(qop[kk]));
     lds_barrier();
+    bool table_bad = false;     // some table entry of the split is out of range
+    if (paged) {
+#pragma unroll
+      for (int i = 0; i < NW; ++i) table_bad |= wave_flag[i] != 0;
+    }
 
-    // ---- pipeline: three chunks in flight in registers while one is computed ------------
-    // Step loc: write chunk loc from its register stage into LDS tile loc % 3, refill that
-    // stage with chunk loc + 3, barrier, compute chunk loc.  Tile loc % 3 was last read by the
-    // compute of chunk loc - 3, which every wave finished before the barrier of step loc - 2.
-    // The scheduler may not reorder the first three issues: stage 0 must be the oldest loads.
+    // ---- pipeline: NST chunks in flight in registers while one is computed -------------
+    // Step loc: write chunk loc from its register stage into LDS tile loc % NLDS, refill that
+    // stage with chunk loc + NST, barrier, compute chunk loc.  The scheduler may not reorder
+    // the first issues: stage 0 must hold the oldest loads in flight.
     issue(I0{}, 0, slot_of(0));
     __builtin_amdgcn_sched_barrier(0);
     issue(I1{}, 1, slot_of(1));
     __builtin_amdgcn_sched_barrier(0);
-    issue(I2{}, 2, slot_of(2));
-    __builtin_amdgcn_sched_barrier(0);
-    auto step = [&](auto st_tag, int loc) __attribute__((always_inline)) {
+    if constexpr (NST > 2) {
+      issue(I2{}, 2, slot_of(2));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (NST > 3) {
+      issue(I3{}, 3, slot_of(3));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    auto step = [&](auto st_tag, int loc, auto edge_tag, auto refresh_tag) __attribute__((always_inline)) {
       constexpr int S = decltype(st_tag)::value;
+      const int slot = stage_slot(st_tag);      // chunk loc's, before the stage is refilled
       commit(st_tag);
-      maybe_refresh_table(loc + PF);
+      maybe_refresh_table(loc + PF, refresh_tag);
       issue(st_tag, loc + PF, slot_of(loc + PF));
       lds_barrier();
-      compute(&lds[S][0], loc, slot_of(loc));
+      compute(&lds[S % NLDS][0], loc, slot, edge_tag);
     };
-    // All three steps run unconditionally (a step past the split computes nothing): with a
-    // conditional step the skipped path would have fewer loads in flight, and the wait counts
-    // at the join would be set for that path.
-    for (int loc = 0; loc < nloc; loc += NBUF) {
-      step(I0{}, loc);
-      step(I1{}, loc + 1);
-      step(I2{}, loc + 2);
+    // The loop body is NST unconditional steps (one per stage), so the same loads are in
+    // flight at every commit and the wait counts stay exact; the last NST - 1 chunks at most
+    // run after it.
+    // Loops of NST steps from loc (a multiple of NST) up to limit (a multiple of NST), then
+    // the last nloc % NST chunks.
+    auto loop = [&](int& loc, int limit, auto edge_tag, auto refresh_tag) __attribute__((always_inline)) {
+      for (; loc < limit; loc += NST) {
+        step(I0{}, loc, edge_tag, refresh_tag);
+        step(I1{}, loc + 1, edge_tag, refresh_tag);
+        if constexpr (NST > 2) step(I2{}, loc + 2, edge_tag, refresh_tag);
+        if constexpr (NST > 3) step(I3{}, loc + 3, edge_tag, refresh_tag);
+      }
+    };
+    auto tail = [&](int loc, auto refresh_tag) __attribute__((always_inline)) {
+      if (loc < nloc) step(I0{}, loc, std::true_type{}, refresh_tag);
+      if constexpr (NST > 2) { if (loc + 1 < nloc) step(I1{}, loc + 1, std::true_type{}, refresh_tag); }
+      if constexpr (NST > 3) { if (loc + 2 < nloc) step(I2{}, loc + 2, std::true_type{}, refresh_tag); }
+    };
+    const int full = nloc - nloc % NST;
+    int loc = 0;
+    if (paged && nloc > kPtCap) {
+      // a split longer than the table slice refreshes it from inside the loop; that load's
+      // wait would lower the wait counts of every step, so these splits have a loop of their own
+      loop(loc, full, std::true_type{}, std::true_type{});
+      tail(loc, std::true_type{});
+    } else {
+      // interior chunks [a, b): at or after every row's window start and the stored range's
+      // start, ending at or before the first query and the stored range's end; the chunks
+      // before and after take the masking path, on boundaries that are multiples of NST
+      int a = 0, b = 0;
+      if (!table_bad) {
+        const int lead = (max(max(lo_last, vlo), 0) + 63) / 64;
+        const int end = max(min(p_first + 1, vhi), 0) / 64;
+        a = min((lead + NST - 1) / NST * NST, full);
+        b = max(a, min(end / NST * NST, full));
+      }
+      loop(loc, a, std::true_type{}, std::false_type{});
+      loop(loc, b, std::false_type{}, std::false_type{});
+      loop(loc, full, std::true_type{}, std::false_type{});
+      tail(loc, std::false_type{});
     }
   }
 
