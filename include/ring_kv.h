@@ -124,6 +124,7 @@ int32_t decode_attn_ref_layout(const rkv_attn_dims* dims, const void* q, const v
  * anything (they are masked and never multiply a result).
  * The span of the window is split into num_splits ranges of whole chunks (0: one chunk
  * per range, every chunk in flight at once) whose partials a log-sum-exp merge combines.
+ * One range spans at most 2^22 chunks (RKV_ERR_SHAPE otherwise).
  * ------------------------------------------------------------------------------- */
 size_t verify_attn_ring_workspace_bytes(const rkv_attn_dims* dims, int32_t ring_size,
                                         int32_t window, int32_t num_splits);
@@ -146,7 +147,8 @@ int32_t verify_attn_ring(const rkv_attn_dims* dims, const void* q, const void* k
  * The key range is split into num_splits ranges of whole chunks (0: chosen from the
  * context and the chip's 256 compute units); each range yields a partial result
  * and a log-sum-exp merge combines them.  Any split gives the same result up to
- * f32 rounding.
+ * f32 rounding.  One split spans at most 2^22 chunks (RKV_ERR_SHAPE otherwise):
+ * with num_splits = 1 that bounds ctx_len by 2^28.
  * ------------------------------------------------------------------------------- */
 size_t verify_attn_paged_workspace_bytes(const rkv_attn_dims* dims, int64_t ctx_len,
                                          int32_t chunk_size, int32_t num_splits);
@@ -164,7 +166,8 @@ int32_t verify_attn_paged_auto_splits(const rkv_attn_dims* dims, int64_t ctx_len
  * The paged call in two phases, for callers that time or distribute them (partials
  * of disjoint key ranges, e.g. computed on different devices, merge the same way).
  * Split s covers logical chunks [s*cps, min((s+1)*cps, n_chunks)) with n_chunks =
- * ceil(ctx_len/64), cps = ceil(n_chunks/num_splits); num_splits >= 1 here.
+ * ceil(ctx_len/64), cps = ceil(n_chunks/num_splits); num_splits >= 1 here, and
+ * cps <= 2^22 (RKV_ERR_SHAPE otherwise).
  *   part_out  [n_kv_heads][num_splits][q_len*G][D] f32: the split's normalised output
  *   part_lse  [n_kv_heads][num_splits][q_len*G]    f32: natural-log lse over the split's
  *             keys, -inf where a row sees no key of the split (then part_out row = 0)

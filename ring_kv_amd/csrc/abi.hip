@@ -83,6 +83,7 @@ int32_t hip_status(hipError_t e) { return e == hipSuccess ? RKV_OK : RKV_ERR_HIP
 
 int32_t run_chunk_attn(ChunkAttnArgs& a, const rkv_attn_dims* d, void* ws, float* out,
                        float* lse, hipStream_t st) {
+  if (a.cps > rkv::kMaxSplitChunks) return RKV_ERR_SHAPE;
   a.out = out;
   a.lse = lse;
   a.part_o = a.part_lse = nullptr;
@@ -342,6 +343,7 @@ int32_t verify_attn_paged_partial(const rkv_attn_dims* dims, const void* q,
   a.num_splits = num_splits;
   a.cps = (int32_t)((a.n_chunks + num_splits - 1) / num_splits);
   if (a.cps < 1) a.cps = 1;
+  if (a.cps > rkv::kMaxSplitChunks) return RKV_ERR_SHAPE;
   a.part_o = part_out;     // partial layout even for one split
   a.part_lse = part_lse;
   return hip_status(rkv::launch_chunk_attn(a, static_cast<hipStream_t>(stream)));

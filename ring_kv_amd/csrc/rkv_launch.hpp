@@ -5,6 +5,10 @@
 
 namespace rkv {
 
+// Most chunks one split may span: positions inside a workgroup are 32-bit offsets from its
+// split's first key.
+constexpr int64_t kMaxSplitChunks = int64_t(1) << 22;
+
 // Attention of one verify block over a chunked KV store (paged pool or position ring),
 // split over ranges of whole chunks.  Rows of a KV head: r = i * G + (h - g * G).
 struct ChunkAttnArgs {

@@ -56,6 +56,14 @@ def test_paged_argument_checks():
     assert paged(splits=-1) == EARG
 
 
+def test_split_span_limit():
+    # one split may span at most 2^22 chunks (positions are 32-bit offsets inside a split)
+    n = (1 << 22) + 1
+    assert paged(n_table=n, n_slots=n, ctx=n * 64, splits=1, ws=NULL, wsb=0) == ESHAPE
+    assert L.verify_attn_paged_partial(dims(), P, P, P, P, n, n, 64, n * 64, 1, P, P, NULL) == ESHAPE
+    assert L.verify_attn_paged_partial(dims(), P, P, P, P, n, n, 64, n * 64, 0, P, P, NULL) == EARG
+
+
 def test_paged_workspace_and_splits():
     d = dims()
     # 4 KV heads: 64 splits of 64 chunks at 262,144 positions; partials [4][64][64][128] f32
