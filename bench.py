@@ -345,7 +345,12 @@ def main():
         log("building the 262,144-context layer")
         c, _ = synth.workload("paged_256k", keep_rows=False)
         t = lambda a: rk.tensor_from_numpy(a, "cuda")  # noqa: E731
-        q, kp, vp, pt = t(c.q), t(c.k_pool), t(c.v_pool), t(c.page_table)
+        q, pt = t(c.q), t(c.page_table)
+        # three copies of the pool in distinct memory, used in turn: each launch reads KV the
+        # previous two did not touch, as consecutive layers of a model would (512 MiB per pool,
+        # twice the last-level cache), so no launch is served from what the last one cached
+        pools = [(t(c.k_pool), t(c.v_pool))]
+        pools += [(pools[0][0].clone(), pools[0][1].clone()) for _ in range(2)]
         kv = c.kv_bytes
         del c
         out = torch.empty((16, 16, 128), dtype=torch.float32, device="cuda")
@@ -356,13 +361,23 @@ def main():
         ws = torch.empty(rk.lib().verify_attn_paged_workspace_bytes(
             ctypes.byref(AttnDims(16, 16, 4, 128, 0.0, 1)), 262144, 64, 0), dtype=torch.uint8,
             device="cuda")
-        fn = lambda: rk.verify_attn_paged(q, kp, vp, pt, 262144, out=out, lse=lse,  # noqa: E731
-                                          workspace=ws)
-        part = lambda: rk.verify_attn_paged_partial(q, kp, vp, pt, 262144, splits,  # noqa: E731
-                                                    part_out=po, part_lse=pl)
+        turn = [0]
+
+        def next_pool():
+            turn[0] += 1
+            return pools[turn[0] % len(pools)]
+
+        def fn():
+            kp, vp = next_pool()
+            rk.verify_attn_paged(q, kp, vp, pt, 262144, out=out, lse=lse, workspace=ws)
+
+        def part():
+            kp, vp = next_pool()
+            rk.verify_attn_paged_partial(q, kp, vp, pt, 262144, splits, part_out=po, part_lse=pl)
+
         for _ in range(max(2, args.warmup)):
             fn()
-        n = max(5, args.steps)
+        n = max(6, args.steps // 3 * 3)      # a multiple of the pool count
         # graph replay, as in the step: n layers per graph, HIP events around the replays
         us = graph_ms(fn, n, 3, torch) * 1e3
         us_split = graph_ms(part, n, 3, torch) * 1e3
@@ -382,7 +397,7 @@ def main():
                                      "frac": round(kv / (us_split * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
                                      "us_per_launch": round(us_split, 2),
                                      "algorithmic_bytes_per_launch": kv, "traffic": None}})
-        del q, kp, vp, pt
+        del q, pt, pools
         torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:

@@ -438,34 +438,45 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
       issue(I3{}, 3, slot_of(3));
       __builtin_amdgcn_sched_barrier(0);
     }
-    auto step = [&](auto st_tag, int loc, auto edge_tag, auto refresh_tag) __attribute__((always_inline)) {
+    auto step = [&](auto st_tag, int loc, auto edge_tag, auto refresh_tag, bool refill) __attribute__((always_inline)) {
       constexpr int S = decltype(st_tag)::value;
       const int slot = stage_slot(st_tag);      // chunk loc's, before the stage is refilled
       commit(st_tag);
       maybe_refresh_table(loc + PF, refresh_tag);
-      issue(st_tag, loc + PF, slot_of(loc + PF));
+      if (refill) issue(st_tag, loc + PF, slot_of(loc + PF));
       lds_barrier();
       compute(&lds[S % NLDS][0], loc, slot, edge_tag);
     };
     // The loop body is NST unconditional steps (one per stage), so the same loads are in
     // flight at every commit and the wait counts stay exact; the last NST - 1 chunks at most
     // run after it.
-    // Loops of NST steps from loc (a multiple of NST) up to limit (a multiple of NST), then
-    // the last nloc % NST chunks.
+    // Loops of NST steps from loc (a multiple of NST) up to limit (a multiple of NST), every
+    // step refilling its stage with a chunk of the split; then the last NST .. 2*NST - 1
+    // chunks, which refill only while chunks remain (no load left in flight at the end).
     auto loop = [&](int& loc, int limit, auto edge_tag, auto refresh_tag) __attribute__((always_inline)) {
       for (; loc < limit; loc += NST) {
-        step(I0{}, loc, edge_tag, refresh_tag);
-        step(I1{}, loc + 1, edge_tag, refresh_tag);
-        if constexpr (NST > 2) step(I2{}, loc + 2, edge_tag, refresh_tag);
-        if constexpr (NST > 3) step(I3{}, loc + 3, edge_tag, refresh_tag);
+        step(I0{}, loc, edge_tag, refresh_tag, true);
+        step(I1{}, loc + 1, edge_tag, refresh_tag, true);
+        if constexpr (NST > 2) step(I2{}, loc + 2, edge_tag, refresh_tag, true);
+        if constexpr (NST > 3) step(I3{}, loc + 3, edge_tag, refresh_tag, true);
       }
     };
     auto tail = [&](int loc, auto refresh_tag) __attribute__((always_inline)) {
-      if (loc < nloc) step(I0{}, loc, std::true_type{}, refresh_tag);
-      if constexpr (NST > 2) { if (loc + 1 < nloc) step(I1{}, loc + 1, std::true_type{}, refresh_tag); }
-      if constexpr (NST > 3) { if (loc + 2 < nloc) step(I2{}, loc + 2, std::true_type{}, refresh_tag); }
+      auto one = [&](auto st_tag, int j) __attribute__((always_inline)) {
+        if (loc + j < nloc)
+          step(st_tag, loc + j, std::true_type{}, refresh_tag, loc + j + NST < nloc);
+      };
+      one(I0{}, 0);
+      one(I1{}, 1);
+      if constexpr (NST == 2) {
+        one(I0{}, 2);
+      } else if constexpr (NST == 3) {
+        one(I2{}, 2); one(I0{}, 3); one(I1{}, 4);
+      } else {
+        one(I2{}, 2); one(I3{}, 3); one(I0{}, 4); one(I1{}, 5); one(I2{}, 6);
+      }
     };
-    const int full = nloc - nloc % NST;
+    const int full = nloc >= NST ? (nloc - NST) / NST * NST : 0;
     int loc = 0;
     if (paged && nloc > kPtCap) {
       // a split longer than the table slice refreshes it from inside the loop; that load's
@@ -498,11 +509,16 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
     float* xo = reinterpret_cast<float*>(&lds[0][0]);          // [NRG][16][D]
     float* xm = xo + NRG * 16 * D;                               // [NRG][16]
     float* xl = xm + NRG * 16;
+    // row (rg, ln), 16-byte column 4t + lq of D/4, XOR-swizzled by the row so that the 16
+    // lanes of one access group (16 rows, same column) land in 16 different bank groups
+    auto xo_off = [&](int t) __attribute__((always_inline)) {
+      return (rg * 16 + ln) * D + (((4 * t + lq) ^ ln) << 2);
+    };
     lds_barrier();
     if (kh == 1 && wave_active) {
 #pragma unroll
       for (int t = 0; t < TMD; ++t)
-        *reinterpret_cast<f32x4*>(&xo[(rg * 16 + ln) * D + 16 * t + 4 * lq]) = oacc[t];
+        *reinterpret_cast<f32x4*>(&xo[xo_off(t)]) = oacc[t];
       if (lq == 0) {
         xm[rg * 16 + ln] = m_run;
         xl[rg * 16 + ln] = l;
@@ -520,7 +536,7 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
       l = a0 * l + a1 * l1;
 #pragma unroll
       for (int t = 0; t < TMD; ++t) {
-        const f32x4 o1 = *reinterpret_cast<const f32x4*>(&xo[(rg * 16 + ln) * D + 16 * t + 4 * lq]);
+        const f32x4 o1 = *reinterpret_cast<const f32x4*>(&xo[xo_off(t)]);
         oacc[t] = oacc[t] * a0 + o1 * a1;
       }
       m_run = M;
