@@ -396,23 +396,49 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
         compute(&lds[0][0], 0, cand, std::false_type{});
     }
   } else {
-    load_q();
+    // The slots of the first NST chunks are read before anything else, and those chunks'
+    // loads go out as soon as these reads return, while the table slice and Q are still on
+    // their way (vector loads complete in order, so waiting for the first reads does not wait
+    // for the later ones).  A paged split would otherwise spend one round trip on its table
+    // before its first chunk load.
+    int first[NST];
+#pragma unroll
+    for (int j = 0; j < NST; ++j)
+      first[j] = paged ? a.pt[c_lo + min(j, nloc - 1)] : slot_of(j);
     // ---- page-table slice in LDS: entry for local chunk loc at pt_lds[loc % kPtCap] ---
-    // Filled once for the first kPtCap chunks; splits longer than that refresh one half of
-    // the slice at a time, 128 chunks before it is needed (and always take the masking path,
-    // as their later entries are not checked here).
-    bool bad = false;
+    // One entry per thread for the first kPtCap chunks; splits longer than that refresh one
+    // half of the slice at a time, 128 chunks before it is needed (and always take the
+    // masking path, as their later entries are not checked here).
+    static_assert(NT == kPtCap, "one table entry per thread");
+    const bool tload = paged && tid < nloc;
+    int tval = 0;
+    if (tload) tval = a.pt[c_lo + tid];
+    load_q();
+
+    // ---- pipeline: NST chunks in flight in registers while one is computed -------------
+    // Step loc: write chunk loc from its register stage into LDS tile loc % NLDS, refill that
+    // stage with chunk loc + NST, barrier, compute chunk loc.  The scheduler may not reorder
+    // the first issues: stage 0 must hold the oldest chunk loads in flight.
+    __builtin_amdgcn_sched_barrier(0);
+    issue(I0{}, 0, __builtin_amdgcn_readfirstlane(first[0]));
+    __builtin_amdgcn_sched_barrier(0);
+    issue(I1{}, 1, __builtin_amdgcn_readfirstlane(first[1]));
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NST > 2) {
+      issue(I2{}, 2, __builtin_amdgcn_readfirstlane(first[2]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (NST > 3) {
+      issue(I3{}, 3, __builtin_amdgcn_readfirstlane(first[3]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (paged) {
-      for (int e = tid; e < kPtCap && e < nloc; e += NT) {
-        const int sl = a.pt[c_lo + e];
-        pt_lds[e] = sl;
-        bad |= (unsigned)sl >= (unsigned)a.n_slots;
-      }
+      if (tload) pt_lds[tid] = tval;
+      const bool bad = tload && (unsigned)tval >= (unsigned)a.n_slots;
       if (lane == 0) wave_flag[w] = __builtin_amdgcn_ballot_w64(bad) != 0;
     }
-    // Q and the table slice are complete before the first chunk load is issued: left
-    // pending, the wait-count analysis would merge them into the chunk loop and drain it at
-    // every use.
+    // Q has arrived before the loop: left pending, the wait-count analysis would merge its
+    // loads into the chunk loop and wait on them at every use.
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(qop[kk]));
     lds_barrier();
@@ -422,22 +448,6 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
       for (int i = 0; i < NW; ++i) table_bad |= wave_flag[i] != 0;
     }
 
-    // ---- pipeline: NST chunks in flight in registers while one is computed -------------
-    // Step loc: write chunk loc from its register stage into LDS tile loc % NLDS, refill that
-    // stage with chunk loc + NST, barrier, compute chunk loc.  The scheduler may not reorder
-    // the first issues: stage 0 must hold the oldest loads in flight.
-    issue(I0{}, 0, slot_of(0));
-    __builtin_amdgcn_sched_barrier(0);
-    issue(I1{}, 1, slot_of(1));
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (NST > 2) {
-      issue(I2{}, 2, slot_of(2));
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if constexpr (NST > 3) {
-      issue(I3{}, 3, slot_of(3));
-      __builtin_amdgcn_sched_barrier(0);
-    }
     auto step = [&](auto st_tag, int loc, auto edge_tag, auto refresh_tag, bool refill) __attribute__((always_inline)) {
       constexpr int S = decltype(st_tag)::value;
       const int slot = stage_slot(st_tag);      // chunk loc's, before the stage is refilled
@@ -575,7 +585,7 @@ hipError_t launch_t(const ChunkAttnArgs& a, hipStream_t stream) {
 
 // Tiles of 64 rows (blockIdx.y), two waves per row group (key halves).  Tiles of one split
 // each read its chunks; a variant with more row groups per workgroup would need more registers
-// than the three register stages leave.
+// than the register stages leave.
 template <int D>
 hipError_t launch_d(const ChunkAttnArgs& a, hipStream_t stream) {
   return launch_t<D, 4, 2>(a, stream);
