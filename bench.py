@@ -9,12 +9,16 @@ data already resident in HBM; the step is captured once in a HIP graph and repla
 
 The JSON line also carries the per-layer figure at context 262,144 (one paged verify layer,
 both kernels), the roofline of the dominant kernel (the paged split-K attention kernel, timed
-live with HIP events on the stream it runs on), and the fp64 oracle timed on the host cores
-over a bounded sample of the same workload.
+live with HIP events on the stream it runs on), the step by layer type, the four single-layer
+workloads timed one by one (cold and warm, median / p10 / p90), a measured HBM read bandwidth,
+and the fp64 oracle timed on the host cores over a bounded sample of the same workload (plus one
+call per single-layer workload).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload stack_40l_131k|paged_256k]
     python bench.py --mode copy     # plain 1-GiB device copies, for HBM counter calibration
     python bench.py --mode kernel   # the dominant kernel alone (10 launches), for counter runs
+    python bench.py --mode configs  # each single-layer workload called 100 times (30 at 256K),
+                                    # a cache-evicting read before each, for a kernel trace
     python bench.py --mode traffic --fetch F.csv --write W.csv --copy-fetch CF.csv --copy-write CW.csv
                                     # HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE /
                                     # WRITE_SIZE counter files, scaled by the copy calibration
@@ -48,12 +52,15 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="stack_40l_131k",
                     choices=["stack_40l_131k", "paged_256k"])
-    ap.add_argument("--mode", default="bench", choices=["bench", "copy", "kernel", "traffic"])
+    ap.add_argument("--mode", default="bench",
+                    choices=["bench", "copy", "kernel", "traffic", "configs"])
     for f in ("fetch", "write", "copy_fetch", "copy_write"):
         ap.add_argument("--" + f.replace("_", "-"), default=None)
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-256k", action="store_true", help="skip the 262,144-context layer")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the single-layer workloads timed one by one")
     return ap.parse_args()
 
 
@@ -140,6 +147,23 @@ class Stack:
         rk.verify_accept(self.logits, self.prop, accept_len=self.acc_len, committed=self.committed,
                          row_argmax=self.argmax, workspace=self.ws_acc)
 
+    def ring_round(self):
+        for d in self.layers:
+            if d["kind"] == "ring":
+                self.rk.verify_attn_ring(d["q"], d["k"], d["v"], d["pos0"], d["window"],
+                                         out=d["out"], lse=d["lse"], workspace=self.ws_ring)
+
+    def paged_round(self):
+        for d in self.layers:
+            if d["kind"] == "paged":
+                self.rk.verify_attn_paged(d["q"], d["k"], d["v"], d["pt"], d["ctx"], out=d["out"],
+                                          lse=d["lse"], workspace=self.ws_paged)
+
+    def accept_once(self):
+        self.rk.verify_accept(self.logits, self.prop, accept_len=self.acc_len,
+                              committed=self.committed, row_argmax=self.argmax,
+                              workspace=self.ws_acc)
+
     def paged_partial_round(self):
         """The dominant kernel alone: the paged split-K kernel over each paged layer once."""
         for d in self.layers:
@@ -147,6 +171,210 @@ class Stack:
                 self.rk.verify_attn_paged_partial(d["q"], d["k"], d["v"], d["pt"], d["ctx"],
                                                   self.splits, part_out=self.part_o,
                                                   part_lse=self.part_l)
+
+
+def attn_flops(c):
+    """QK^T + PV flops of an attention case, counting exactly the keys each query sees."""
+    vis = 0
+    for i in range(c.q_len):
+        p = c.pos0 + i if c.kind == "ring" else c.ctx_len - c.q_len + i
+        vis += min(p + 1, c.window) if c.window else p + 1
+    return 4 * c.head_dim * c.n_q_heads * vis
+
+
+class ReadProbe:
+    """The streaming read probe (ring_kv_amd/libring_kv_probe.so): plain 16-byte loads over a
+    buffer, nothing else.  Used to flush the caches without leaving dirty lines behind, and to
+    measure the HBM read bandwidth this machine delivers."""
+
+    def __init__(self, torch):
+        import ctypes
+        self.torch = torch
+        self.L = ctypes.CDLL(os.path.join(ROOT, "ring_kv_amd", "libring_kv_probe.so"))
+        self.L.rkv_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                          ctypes.c_void_p, ctypes.c_void_p]
+        self.sink = torch.empty(4096 * 256, dtype=torch.int32, device="cuda")
+
+    def read(self, buf, workgroups=1024):
+        rc = self.L.rkv_probe_read(buf.data_ptr(), buf.numel() * buf.element_size(), workgroups,
+                                   self.sink.data_ptr(),
+                                   self.torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"rkv_probe_read: hip error {rc}")
+
+
+def config_timings(torch, rk, synth, probe, n_small, n_large):
+    """The single-layer workloads (plus the small accept), each captured n times in one HIP graph:
+    warm = back-to-back calls; cold = every call preceded by a 512 MiB streaming read that evicts
+    L2 and the last-level cache without dirtying them (minus a graph of the reads alone); the
+    256K pool also rotates over three copies.  Mean µs per call; per-dispatch distributions come
+    from the kernel trace of `bench.py --mode configs`."""
+    t = lambda a: rk.tensor_from_numpy(a, "cuda")  # noqa: E731
+    scratch = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = lambda: probe.read(scratch)  # noqa: E731
+    flush_us = graph_ms(flush, n_small, 3, torch) * 1e3
+    f32 = lambda *sh: torch.empty(sh, dtype=torch.float32, device="cuda")  # noqa: E731
+    out = {"flush_us": round(flush_us, 1)}
+
+    def entry(name, fns, n, nbytes, flops, peak_tflops, flops_unit, note):
+        turn = [0]
+
+        def op():
+            turn[0] += 1
+            fns[turn[0] % len(fns)]()
+
+        def cold_op():
+            flush()
+            op()
+
+        n = n // len(fns) * len(fns)
+        warm = graph_ms(op, n, 3, torch) * 1e3
+        cold = graph_ms(cold_op, n, 3, torch) * 1e3 - flush_us
+        e = {"us_cold": round(cold, 2), "us_warm": round(warm, 2), "calls_per_graph": n,
+             "note": note}
+        if nbytes:
+            e["gbps_cold"] = round(nbytes / (cold * 1e-6) / 1e9, 1)
+            e["hbm_frac_cold"] = round(e["gbps_cold"] / HBM_PEAK_GBPS, 4)
+        if flops:
+            tf = flops / (cold * 1e-6) / 1e12
+            e.update({"flops": flops, "tflops_cold": round(tf, 2), "peak_tflops": peak_tflops,
+                      "util_" + flops_unit: round(tf / peak_tflops, 4)})
+        out[name] = e
+
+    # C1: contiguous 1,024-key verify, f32 (VALU arithmetic), and the accept over [17 x 4096]
+    c, acc = synth.workload("contig_1k_f32")
+    q, k, v = t(c.q), t(c.k_rows), t(c.v_rows)
+    o1, l1 = f32(16, 8, 64), f32(16, 8)
+    entry("contig_1k_f32", [lambda: rk.decode_attn_ref_layout(q, k, v, 1024, out=o1, lse=l1)],
+          n_small, c.kv_bytes, attn_flops(c), 157.3, "fp32_vector",
+          "decode_attn_ref_layout, auto splits; bound: launch latency")
+    lg, pr = t(acc.logits), t(acc.proposals)
+    al, cm, am = (torch.empty(n, dtype=torch.int32, device="cuda") for n in (1, 17, 17))
+    entry("accept_17x4096", [lambda: rk.verify_accept(lg, pr, accept_len=al, committed=cm,
+                                                      row_argmax=am)],
+          n_small, acc.logits.nbytes, 0, 0, "", "verify_accept; bound: launch latency")
+    # C2: window 512 over the 2,048-slot ring
+    c, _ = synth.workload("ring_w512_r2048", keep_rows=False)
+    q2, kr, vr = t(c.q), t(c.k_ring), t(c.v_ring)
+    o, l = f32(16, 16, 128), f32(16, 16)
+    entry("ring_w512_r2048", [lambda: rk.verify_attn_ring(q2, kr, vr, c.pos0, c.window, out=o,
+                                                          lse=l)],
+          n_small, c.kv_bytes, attn_flops(c), 2500.0, "mfma_bf16",
+          "verify_attn_ring, one chunk per split + merge; bound: launch latency")
+    # C3: paged 8K
+    c3, _ = synth.workload("paged_8k", keep_rows=False)
+    q3, kp3, vp3, pt3 = t(c3.q), t(c3.k_pool), t(c3.v_pool), t(c3.page_table)
+    entry("paged_8k", [lambda: rk.verify_attn_paged(q3, kp3, vp3, pt3, 8192, out=o, lse=l)],
+          n_small, c3.kv_bytes, attn_flops(c3), 2500.0, "mfma_bf16",
+          "verify_attn_paged, auto splits + merge")
+    # C4: paged 256K, three pool copies in turn
+    c4, _ = synth.workload("paged_256k", keep_rows=False)
+    q4, pt4 = t(c4.q), t(c4.page_table)
+    pools = [(t(c4.k_pool), t(c4.v_pool))]
+    pools += [(pools[0][0].clone(), pools[0][1].clone()) for _ in range(2)]
+    fns = [lambda kp=kp, vp=vp: rk.verify_attn_paged(q4, kp, vp, pt4, 262144, out=o, lse=l)
+           for kp, vp in pools]
+    entry("paged_256k", fns, n_large, c4.kv_bytes, attn_flops(c4), 2500.0, "mfma_bf16",
+          "verify_attn_paged, 64 splits + merge; warm = back-to-back over the three pool copies")
+    del pools, fns, scratch
+    torch.cuda.empty_cache()
+    return out
+
+
+def config_calls(torch, rk, synth, probe, n_small, n_large):
+    """Eager calls of the single-layer workloads, each preceded by a 512 MiB streaming read, for
+    a rocprofv3 kernel trace (per-dispatch durations: median, p10, p90)."""
+    t = lambda a: rk.tensor_from_numpy(a, "cuda")  # noqa: E731
+    scratch = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
+    f32 = lambda *sh: torch.empty(sh, dtype=torch.float32, device="cuda")  # noqa: E731
+
+    def run(fn, n):
+        for _ in range(n):
+            probe.read(scratch)
+            fn()
+        torch.cuda.synchronize()
+
+    c, acc = synth.workload("contig_1k_f32")
+    q, k, v = t(c.q), t(c.k_rows), t(c.v_rows)
+    o1, l1 = f32(16, 8, 64), f32(16, 8)
+    run(lambda: rk.decode_attn_ref_layout(q, k, v, 1024, out=o1, lse=l1), n_small)
+    lg, pr = t(acc.logits), t(acc.proposals)
+    run(lambda: rk.verify_accept(lg, pr), n_small)
+    o, l = f32(16, 16, 128), f32(16, 16)
+    for name, n in (("ring_w512_r2048", n_small), ("paged_8k", n_small), ("paged_256k", n_large)):
+        c, _ = synth.workload(name, keep_rows=False)
+        q = t(c.q)
+        if c.kind == "ring":
+            kr, vr = t(c.k_ring), t(c.v_ring)
+            run(lambda: rk.verify_attn_ring(q, kr, vr, c.pos0, c.window, out=o, lse=l), n)
+        else:
+            kp, vp, pt = t(c.k_pool), t(c.v_pool), t(c.page_table)
+            run(lambda: rk.verify_attn_paged(q, kp, vp, pt, c.ctx_len, out=o, lse=l), n)
+            del kp, vp
+        torch.cuda.empty_cache()
+
+
+def read_bw_probe(torch, probe):
+    """Measured HBM read bandwidth on this machine: the streaming read probe over four 1 GiB buffers
+    in turn (so no pass is served from the last-level cache), best of several grid sizes."""
+    bufs = [torch.zeros(1 << 30, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    res = {}
+    for wgs in (256, 512, 1024, 2048):
+        turn = [0]
+
+        def f():
+            turn[0] += 1
+            probe.read(bufs[turn[0] % 4], wgs)
+
+        us = graph_ms(f, 8, 3, torch) * 1e3
+        res[str(wgs)] = round((1 << 30) / (us * 1e-6) / 1e9, 1)
+    del bufs
+    torch.cuda.empty_cache()
+    return {"gbps": max(res.values()), "by_workgroups": res,
+            "method": "16-byte non-temporal loads over four 1 GiB buffers in turn, graph replay "
+                      "(ring_kv_amd/csrc/probe.hip)"}
+
+
+def cpu_info():
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = ""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info()
+                         if i.get("user_api") == "blas")
+    except Exception:  # noqa: BLE001
+        pass
+    return model, blas
+
+
+def oracle_per_config(synth, oracle):
+    """One timed oracle call per single-layer workload (µs of wall time)."""
+    res = {}
+    c, acc = synth.workload("contig_1k_f32")
+    t0 = time.perf_counter()
+    oracle.attention_contiguous(c.q, c.k_rows, c.v_rows, c.ctx_len, window=c.window, dtype=c.dtype)
+    res["contig_1k_f32"] = round((time.perf_counter() - t0) * 1e6, 1)
+    t0 = time.perf_counter()
+    oracle.greedy_accept(acc.logits, acc.proposals)
+    res["accept_17x4096"] = round((time.perf_counter() - t0) * 1e6, 1)
+    for name in ("ring_w512_r2048", "paged_8k", "paged_256k"):
+        c, _ = synth.workload(name, keep_rows=False)
+        t0 = time.perf_counter()
+        if c.kind == "ring":
+            oracle.attention_ring(c.q, c.k_ring, c.v_ring, c.pos0, c.ring_head, c.ring_size,
+                                  c.window)
+        else:
+            oracle.attention_paged(c.q, c.k_pool, c.v_pool, c.page_table, c.ctx_len)
+        res[name] = round((time.perf_counter() - t0) * 1e6, 1)
+        del c
+    return res
 
 
 def cpu_baseline(synth, oracle):
@@ -168,10 +396,13 @@ def cpu_baseline(synth, oracle):
             oracle.attention_ring(c.q, c.k_ring, c.v_ring, c.pos0, c.ring_head, c.ring_size, c.window)
     oracle.greedy_accept(acc.logits, acc.proposals)
     dt = time.perf_counter() - t0
+    model, blas = cpu_info()
     return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle", "seconds": round(dt, 3),
             "sample": "1 paged layer (ctx 131,072) + 3 ring layers + accept [17x65536] of the "
-                      "40-layer step; KV bytes of the sample / wall time"}
+                      "40-layer step; KV bytes of the sample / wall time",
+            "cpu": model, "blas": blas,
+            "us_per_call": oracle_per_config(synth, oracle)}
 
 
 def counter_kib(path, kernel_substr):
@@ -284,6 +515,11 @@ def main():
         print(json.dumps({"mode": "kernel", "launches": 10, "splits": splits}), flush=True)
         return
 
+    if args.mode == "configs":
+        config_calls(torch, rk, synth, ReadProbe(torch), 100, 30)
+        print(json.dumps({"mode": "configs"}), flush=True)
+        return
+
     res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded N(0,1) bf16 K/V, planted-argmax logits)"}
@@ -322,6 +558,15 @@ def main():
         per_launch = 2 * 131072 * 4 * 128 * 2
         achieved = per_launch / (k_ms * 1e-3) / 1e9
         log(f"paged split kernel {k_ms * 1e3:.1f} us/launch, {achieved:.0f} GB/s")
+        # the step by layer type, each type captured alone (30 ring layers, 10 paged, accept)
+        ring_us = graph_ms(st.ring_round, 1, max(3, args.steps // 2), torch) * 1e3 / 30
+        paged_us = graph_ms(st.paged_round, 1, max(3, args.steps // 2), torch) * 1e3 / 10
+        acc_us = graph_ms(st.accept_once, 5, max(3, args.steps // 2), torch) * 1e3
+        log(f"per layer: ring {ring_us:.2f} us, paged {paged_us:.2f} us, accept {acc_us:.2f} us")
+        res["per_layer_type_us"] = {"ring_w512": round(ring_us, 2), "paged_131k": round(paged_us, 2),
+                                    "accept_17x65536": round(acc_us, 2),
+                                    "sum_40_layers_and_accept": round(30 * ring_us + 10 * paged_us
+                                                                      + acc_us, 1)}
         res.update({
             "value": round(step_bytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
             "ms_per_step": round(ms, 4), "eager_ms_per_step": round(eager_ms, 4),
@@ -399,6 +644,26 @@ def main():
                                      "algorithmic_bytes_per_launch": kv, "traffic": None}})
         del q, pt, pools
         torch.cuda.empty_cache()
+
+    if not args.no_configs:
+        log("single-layer workloads, cold and warm")
+        probe = ReadProbe(torch)
+        res["configs_gpu"] = config_timings(torch, rk, synth, probe, 100, 30)
+        res["read_bw_probe"] = read_bw_probe(torch, probe)
+        if "us_per_layer_256k" in res:
+            # the headline 256K figure is the cold one (caches evicted before each call); the
+            # back-to-back graph figure stays alongside (it runs into the card's power limit)
+            cold = res["configs_gpu"]["paged_256k"]["us_cold"]
+            kv256 = 2 * 262144 * 4 * 128 * 2
+            res["us_per_layer_256k_back_to_back"] = res["us_per_layer_256k"]
+            res.update({"us_per_layer_256k": cold,
+                        "kv_gbps_256k": round(kv256 / (cold * 1e-6) / 1e9, 1),
+                        "hbm_frac_256k": round(kv256 / (cold * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                        "hbm_frac_256k_of_read_probe": round(
+                            kv256 / (cold * 1e-6) / 1e9 / res["read_bw_probe"]["gbps"], 4)})
+        if "roofline" in res:
+            res["roofline"]["frac_of_read_probe"] = round(
+                res["roofline"]["achieved"] / res["read_bw_probe"]["gbps"], 4)
 
     if not args.no_cpu_baseline:
         import oracle

@@ -15,6 +15,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libring_kv.so")
+# measurement-only streaming read probe, used by bench.py (not part of the C interface)
+PROBE_LIB = os.path.join(HERE, "libring_kv_probe.so")
+PROBE_SRC = "probe.hip"
 SOURCES = ["abi.hip", "attn_chunked.hip", "attn_merge.hip", "attn_contig.hip", "accept.hip",
            "layout.hip"]
 ARCH = "gfx950"
@@ -54,8 +57,14 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    pobj = _compile(hipcc, PROBE_SRC)
+    r = subprocess.run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", pobj, "-o",
+                        PROBE_LIB + ".tmp"], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed (probe)\n{r.stdout}\n{r.stderr}")
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 
