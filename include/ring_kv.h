@@ -224,6 +224,67 @@ int32_t ref_layout_to_paged(const void* k_src, const void* v_src, int64_t pos_fi
                             int32_t n_table, int32_t n_slots, int32_t chunk_size,
                             void* stream);
 
+/* ---------------------------------------------------------------------------------
+ * KV append and rollback for the verify block.  Before verify attention the block's own
+ * n K/V rows (positions ctx .. ctx+n-1) join the stores; after the accept, the a+1 kept
+ * rows are committed and the rest are left to be overwritten (lucebox post, "3. Ring
+ * caches for the sliding-window layers": slot = pos mod 2048; "Three optimizations",
+ * item 1: a pool of 64-token chunks located through a page table; the verify step
+ * commits only the tokens the target itself would emit).
+ *
+ * Ring: verify_kv_append_ring writes row i (position pos_first+i) at ring slot
+ * (pos_first+i) mod ring_size, 1 <= n <= RKV_MAX_APPEND, n <= ring_size.  Rolling back
+ * needs no call: a rejected position is written again by the next block's append before
+ * any attention reads it.
+ *
+ * Pool: a host-side pager owns the free list of pool slots and a host copy of the page
+ * table; ctx is its committed length.
+ *   rkv_pager_reserve(p, n, &first_chunk, &n_new, slots)  allocates slots for the chunks
+ *       that positions ctx .. ctx+n-1 start: chunks first_chunk .. first_chunk+n_new-1
+ *       (first_chunk = ceil(ctx/64)) get slots[0 .. n_new-1] (capacity
+ *       RKV_MAX_APPEND_CHUNKS).  One block may be pending at a time.
+ *   verify_kv_append_paged(...)  writes those table entries into the device page table and
+ *       the n rows into the pool, in one launch (positions in chunks below first_chunk use
+ *       the device table's existing entries).
+ *   rkv_pager_commit(p, n_keep)  the first n_keep rows of the pending block are committed
+ *       (ctx += n_keep, 0 <= n_keep <= n); its chunks that hold no committed position go
+ *       back to the free list, and their host table entries become -1.
+ * Slots come from a stack that starts as 0, 1, 2, ...; freed slots are reused first, the
+ * most recently freed one first.  Status: RKV_ERR_TABLE when the free list or the table
+ * cannot cover the block (nothing changes), RKV_ERR_ARG for a reserve while a block is
+ * pending, a commit without one, n out of range or n_keep > n, RKV_ERR_NULL for null
+ * pointers.  A pager is host memory only and not thread-safe; destroy it with
+ * rkv_pager_destroy.
+ * ------------------------------------------------------------------------------- */
+#define RKV_MAX_APPEND 1024
+#define RKV_MAX_APPEND_CHUNKS 17        /* a block of 1024 rows starts at most 17 chunks */
+
+typedef struct rkv_pager rkv_pager;
+rkv_pager* rkv_pager_create(int32_t n_slots, int32_t n_table);   /* NULL on sizes < 1 */
+void rkv_pager_destroy(rkv_pager* p);
+int64_t rkv_pager_ctx_len(const rkv_pager* p);                    /* -1 for NULL */
+int32_t rkv_pager_free_slots(const rkv_pager* p);                 /* -1 for NULL */
+/* host copy of table entries 0 .. n-1 into out (-1: no slot); n <= n_table */
+int32_t rkv_pager_table(const rkv_pager* p, int32_t* out, int32_t n);
+int32_t rkv_pager_reserve(rkv_pager* p, int32_t n, int32_t* first_chunk, int32_t* n_new,
+                          int32_t* slots);
+int32_t rkv_pager_commit(rkv_pager* p, int32_t n_keep);
+
+/* k_new, v_new [n][Hkv][D] bf16 (device), the rows of positions pos_first .. */
+int32_t verify_kv_append_ring(const void* k_new, const void* v_new, int32_t n,
+                              int64_t pos_first, int32_t n_kv_heads, int32_t head_dim,
+                              void* k_ring, void* v_ring, int32_t ring_size, void* stream);
+/* rows of positions ctx_len .. ctx_len+n-1; first_chunk must be ceil(ctx_len/64) and n_new
+ * the number of chunks the block starts (as rkv_pager_reserve reports them); new_slots is a
+ * host array of n_new slots in [0, n_slots); page_table is the device table (written for the
+ * new chunks).  RKV_ERR_TABLE if the block does not fit the table or the slots are out of
+ * range. */
+int32_t verify_kv_append_paged(const void* k_new, const void* v_new, int32_t n,
+                               int64_t ctx_len, int32_t n_kv_heads, int32_t head_dim,
+                               void* k_pool, void* v_pool, int32_t* page_table,
+                               int32_t n_table, int32_t n_slots, int32_t first_chunk,
+                               int32_t n_new, const int32_t* new_slots, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

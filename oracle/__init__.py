@@ -20,6 +20,10 @@ What it computes, and where the method is stated:
 * ``accept``: greedy acceptance, committing the longest drafted prefix on which
   the target's argmax agrees plus the target's next token (same post, "TL;DR" and
   "The model, fast MoE with a drafter in the box": exact greedy equivalence).
+* ``cache``: appending the verify block's own K/V rows to the ring and the pool
+  before its attention, and committing the accepted ones (slot = pos mod 2048; a
+  pool chunk gets a slot when first written and gives it back if the block's rows
+  in it are all rejected), with ``PagerModel``, the slot bookkeeping.
 
 Parity pins: every function here is pinned in ``tests/test_oracle_*.py`` by
 closed forms, invariants, brute force or a library routine; none is "parity
@@ -30,3 +34,4 @@ from .attention import (attend_rows, attention_contiguous, attention_paged,  # n
                         key_bounds, to_f64)
 from .merge import attention_partial, lse_merge  # noqa: F401
 from .accept import first_argmax, greedy_accept  # noqa: F401
+from .cache import PagerModel, append_paged, append_ring  # noqa: F401

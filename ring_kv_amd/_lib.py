@@ -52,6 +52,17 @@ _PROTOS = {
                                      _P, c_int32, _P]),
     "ref_layout_to_paged": (c_int32, [_P, _P, c_int64, c_int64, c_int32, c_int32, c_int32, _P,
                                       _P, _P, c_int32, c_int32, c_int32, _P]),
+    "rkv_pager_create": (c_void_p, [c_int32, c_int32]),
+    "rkv_pager_destroy": (None, [c_void_p]),
+    "rkv_pager_ctx_len": (c_int64, [c_void_p]),
+    "rkv_pager_free_slots": (c_int32, [c_void_p]),
+    "rkv_pager_table": (c_int32, [c_void_p, _P, c_int32]),
+    "rkv_pager_reserve": (c_int32, [c_void_p, c_int32, _P, _P, _P]),
+    "rkv_pager_commit": (c_int32, [c_void_p, c_int32]),
+    "verify_kv_append_ring": (c_int32, [_P, _P, c_int32, c_int64, c_int32, c_int32, _P, _P,
+                                        c_int32, _P]),
+    "verify_kv_append_paged": (c_int32, [_P, _P, c_int32, c_int64, c_int32, c_int32, _P, _P, _P,
+                                         c_int32, c_int32, c_int32, c_int32, _P, _P]),
 }
 
 _lib = None
@@ -61,8 +72,9 @@ def declared_functions() -> list[str]:
     """Function names the public header declares."""
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int32_t|size_t|char\s*\*|const char\s*\*)\s*\**\s*(\w+)\s*\(",
-                                 text, flags=re.M)))
+    return sorted(set(re.findall(
+        r"^\s*(?:const\s+)?(?:int32_t|int64_t|size_t|void|rkv_pager|char)\s*\**\s*(\w+)\s*\(",
+        text, flags=re.M)))
 
 
 def lib() -> ctypes.CDLL:

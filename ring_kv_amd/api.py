@@ -14,6 +14,7 @@ import torch
 from ._lib import RKV_BF16, RKV_F32, AttnDims, check, lib
 
 CHUNK = 64
+RKV_MAX_APPEND_CHUNKS = 17
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -237,6 +238,82 @@ def ref_layout_to_paged(k_src, v_src, pos_first: int, k_pool, v_pool, page_table
     check("ref_layout_to_paged", lib().ref_layout_to_paged(
         _ptr(k_src), _ptr(v_src), pos_first, n, hkv, d, RKV_BF16, _ptr(k_pool), _ptr(v_pool),
         _ptr(page_table), page_table.numel(), k_pool.shape[0], CHUNK, _stream(stream, dev)))
+
+
+class Pager:
+    """The library's host-side pager of a paged pool (rkv_pager_*): slot free list and a host
+    copy of the page table for one sequence; reserve -> append -> commit per verify block."""
+
+    def __init__(self, n_slots: int, n_table: int):
+        self._L = lib()
+        self._p = self._L.rkv_pager_create(n_slots, n_table)
+        if not self._p:
+            raise ValueError("rkv_pager_create: sizes must be >= 1")
+        self.n_slots, self.n_table = n_slots, n_table
+
+    def close(self):
+        if self._p:
+            self._L.rkv_pager_destroy(self._p)
+            self._p = None
+
+    def __del__(self):
+        self.close()
+
+    @property
+    def ctx_len(self) -> int:
+        return int(self._L.rkv_pager_ctx_len(self._p))
+
+    @property
+    def free_slots(self) -> int:
+        return int(self._L.rkv_pager_free_slots(self._p))
+
+    def table(self, n: Optional[int] = None):
+        """Host copy of the first n table entries (-1: no slot) as a list."""
+        n = self.n_table if n is None else n
+        buf = (ctypes.c_int32 * max(1, n))()
+        check("rkv_pager_table", self._L.rkv_pager_table(self._p, buf, n))
+        return list(buf)[:n]
+
+    def reserve(self, n: int):
+        """Slots for the chunks the next n positions start: (first_chunk, [slots])."""
+        first, k = ctypes.c_int32(), ctypes.c_int32()
+        slots = (ctypes.c_int32 * RKV_MAX_APPEND_CHUNKS)()
+        check("rkv_pager_reserve", self._L.rkv_pager_reserve(
+            self._p, n, ctypes.byref(first), ctypes.byref(k), slots))
+        return first.value, list(slots)[:k.value]
+
+    def commit(self, n_keep: int):
+        check("rkv_pager_commit", self._L.rkv_pager_commit(self._p, n_keep))
+
+
+def verify_kv_append_ring(k_new, v_new, pos_first: int, k_ring, v_ring, *, stream=None):
+    """Append a verify block's rows k_new, v_new [n][Hkv][D] (positions pos_first..) to the
+    ring at slot pos mod ring_size."""
+    _need(k_new, "k_new", torch.bfloat16, 3)
+    dev = k_new.device
+    for t, nm in ((v_new, "v_new"), (k_ring, "k_ring"), (v_ring, "v_ring")):
+        _need(t, nm, torch.bfloat16, 4 if nm != "v_new" else 3, dev)
+    n, hkv, d = k_new.shape
+    check("verify_kv_append_ring", lib().verify_kv_append_ring(
+        _ptr(k_new), _ptr(v_new), n, pos_first, hkv, d, _ptr(k_ring), _ptr(v_ring),
+        k_ring.shape[0] * CHUNK, _stream(stream, dev)))
+
+
+def verify_kv_append_paged(k_new, v_new, ctx_len: int, k_pool, v_pool, page_table,
+                           first_chunk: int, new_slots, *, stream=None):
+    """Append a verify block's rows (positions ctx_len..) to the pool; the chunks the block
+    starts (from Pager.reserve) get new_slots, written into the device page table too."""
+    _need(k_new, "k_new", torch.bfloat16, 3)
+    dev = k_new.device
+    for t, nm in ((v_new, "v_new"), (k_pool, "k_pool"), (v_pool, "v_pool")):
+        _need(t, nm, torch.bfloat16, 4 if nm != "v_new" else 3, dev)
+    _need(page_table, "page_table", torch.int32, 1, dev)
+    n, hkv, d = k_new.shape
+    slots = (ctypes.c_int32 * max(1, len(new_slots)))(*new_slots)
+    check("verify_kv_append_paged", lib().verify_kv_append_paged(
+        _ptr(k_new), _ptr(v_new), n, ctx_len, hkv, d, _ptr(k_pool), _ptr(v_pool),
+        _ptr(page_table), page_table.numel(), k_pool.shape[0], first_chunk, len(new_slots),
+        slots, _stream(stream, dev)))
 
 
 def tensor_from_numpy(arr, device="cuda", bf16_bits: Optional[bool] = None) -> torch.Tensor:

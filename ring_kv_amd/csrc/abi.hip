@@ -462,4 +462,67 @@ int32_t ref_layout_to_paged(const void* k_src, const void* v_src, int64_t pos_fi
   return hip_status(rkv::launch_scatter(a, static_cast<hipStream_t>(stream)));
 }
 
+// ---- KV append of a verify block -------------------------------------------------------
+
+int32_t verify_kv_append_ring(const void* k_new, const void* v_new, int32_t n,
+                              int64_t pos_first, int32_t n_kv_heads, int32_t head_dim,
+                              void* k_ring, void* v_ring, int32_t ring_size, void* stream) {
+  if (k_new == nullptr || v_new == nullptr || k_ring == nullptr || v_ring == nullptr)
+    return RKV_ERR_NULL;
+  if (n_kv_heads < 1 || (head_dim != 64 && head_dim != 128)) return RKV_ERR_SHAPE;
+  if (n < 1 || n > RKV_MAX_APPEND || pos_first < 0) return RKV_ERR_ARG;
+  if (ring_size < kChunk || ring_size % kChunk != 0 || n > ring_size) return RKV_ERR_RING;
+  rkv::ScatterArgs a{};
+  a.k_src = static_cast<const uint16_t*>(k_new);
+  a.v_src = static_cast<const uint16_t*>(v_new);
+  a.pos_first = pos_first;
+  a.n = n;
+  a.n_kv_heads = n_kv_heads;
+  a.head_dim = head_dim;
+  a.k_dst = static_cast<uint16_t*>(k_ring);
+  a.v_dst = static_cast<uint16_t*>(v_ring);
+  a.pt = nullptr;
+  a.n_slots = ring_size / kChunk;
+  a.ring_size = ring_size;
+  return hip_status(rkv::launch_scatter(a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t verify_kv_append_paged(const void* k_new, const void* v_new, int32_t n,
+                               int64_t ctx_len, int32_t n_kv_heads, int32_t head_dim,
+                               void* k_pool, void* v_pool, int32_t* page_table,
+                               int32_t n_table, int32_t n_slots, int32_t first_chunk,
+                               int32_t n_new, const int32_t* new_slots, void* stream) {
+  if (k_new == nullptr || v_new == nullptr || k_pool == nullptr || v_pool == nullptr ||
+      page_table == nullptr || (n_new > 0 && new_slots == nullptr))
+    return RKV_ERR_NULL;
+  if (n_kv_heads < 1 || (head_dim != 64 && head_dim != 128)) return RKV_ERR_SHAPE;
+  if (n < 1 || n > RKV_MAX_APPEND || ctx_len < 0) return RKV_ERR_ARG;
+  if (n_slots < 1 || n_table < 1) return RKV_ERR_TABLE;
+  const int64_t c0 = (ctx_len + kChunk - 1) / kChunk;
+  const int64_t c1 = (ctx_len + n + kChunk - 1) / kChunk;
+  if (c1 > n_table) return RKV_ERR_TABLE;
+  if (first_chunk != c0 || n_new != c1 - c0 || n_new > RKV_MAX_APPEND_CHUNKS) return RKV_ERR_ARG;
+  rkv::ScatterArgs a{};
+  for (int32_t i = 0; i < n_new; ++i) {
+    if (new_slots[i] < 0 || new_slots[i] >= n_slots) return RKV_ERR_TABLE;
+    a.new_slots[i] = new_slots[i];
+  }
+  a.k_src = static_cast<const uint16_t*>(k_new);
+  a.v_src = static_cast<const uint16_t*>(v_new);
+  a.pos_first = ctx_len;
+  a.n = n;
+  a.n_kv_heads = n_kv_heads;
+  a.head_dim = head_dim;
+  a.k_dst = static_cast<uint16_t*>(k_pool);
+  a.v_dst = static_cast<uint16_t*>(v_pool);
+  a.pt = page_table;
+  a.n_table = n_table;
+  a.n_slots = n_slots;
+  a.ring_size = 0;
+  a.pt_w = page_table;
+  a.first_new = first_chunk;
+  a.n_new = n_new;
+  return hip_status(rkv::launch_scatter(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -1,4 +1,5 @@
-// Contiguous rows -> chunked KV store (ring or paged pool).  Position p of the rows goes to
+// Contiguous rows -> chunked KV store (ring or paged pool); also the append of a verify block's
+// own rows.  Position p of the rows goes to
 // ring slot p mod ring_size (lucebox post "Laguna XS 2.1 33B on a RTX 3090: 296 tok/s peak,
 // 152 tok/s at 256K context", "3. Ring caches for the sliding-window layers") or to pool slot
 // page_table[p / 64] ("Three optimizations", item 1), offset p mod 64; K key-major and V
@@ -12,6 +13,7 @@ namespace {
 __global__ __launch_bounds__(256) void scatter_kernel(ScatterArgs a) {
   const int64_t total = a.n * a.n_kv_heads * a.head_dim;
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (a.pt_w != nullptr && e < a.n_new) a.pt_w[a.first_new + e] = a.new_slots[e];
   if (e >= total) return;
   const int d = (int)(e % a.head_dim);
   const int g = (int)((e / a.head_dim) % a.n_kv_heads);
@@ -25,7 +27,9 @@ __global__ __launch_bounds__(256) void scatter_kernel(ScatterArgs a) {
   } else {
     const int64_t c = pos / kChunk;
     if (c >= a.n_table) return;
-    slot = a.pt[c];
+    // a chunk the appended block starts takes its new slot (its table entry is being
+    // written by this launch); older chunks read the table
+    slot = (a.pt_w != nullptr && c >= a.first_new) ? a.new_slots[c - a.first_new] : a.pt[c];
     if (slot < 0 || slot >= a.n_slots) return;
     off = pos % kChunk;
   }

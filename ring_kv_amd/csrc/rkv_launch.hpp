@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ring_kv.h"
+
 namespace rkv {
 
 // Most chunks one split may span: positions inside a workgroup are 32-bit offsets from its
@@ -90,6 +92,11 @@ struct ScatterArgs {
   int32_t n_table;        // page table entries (paged)
   int32_t n_slots;        // pool slots, or ring chunk slots
   int64_t ring_size;
+  // append of a verify block to the pool: chunks first_new .. first_new+n_new-1 take
+  // new_slots[] (and pt_w, the writable table, gets those entries); others read pt
+  int32_t* pt_w;          // nullptr: no table writes
+  int32_t first_new, n_new;
+  int32_t new_slots[RKV_MAX_APPEND_CHUNKS];
 };
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t stream);
 

@@ -125,3 +125,24 @@ def test_layout_helper_checks():
     assert L.ref_layout_to_paged(P, P, 0, 8193, 4, 128, 1, P, P, P, 128, 128, 64, NULL) == ETABLE
     assert L.ref_layout_to_paged(P, P, 0, 10, 4, 96, 1, P, P, P, 128, 128, 64, NULL) == ESHAPE
     assert L.ref_layout_to_paged(NULL, P, 0, 0, 4, 128, 1, P, P, P, 128, 128, 64, NULL) == OK
+
+
+def test_append_checks():
+    app_r = lambda n=16, pos=100, hkv=4, d=128, size=2048, k=P: L.verify_kv_append_ring(  # noqa: E731
+        k, P, n, pos, hkv, d, P, P, size, NULL)
+    assert app_r(k=NULL) == ENULL
+    assert app_r(d=96) == ESHAPE and app_r(hkv=0) == ESHAPE
+    assert app_r(n=0) == EARG and app_r(n=1025) == EARG and app_r(pos=-1) == EARG
+    assert app_r(size=100) == ERING and app_r(n=200, size=128) == ERING
+    slots = (ctypes.c_int32 * 2)(5, 6)
+
+    def app_p(n=16, ctx=120, first=2, n_new=1, sl=slots, table=P, n_table=10, n_slots=8):
+        return L.verify_kv_append_paged(P, P, n, ctx, 4, 128, P, P, table, n_table, n_slots,
+                                        first, n_new, sl, NULL)
+    assert app_p(table=NULL) == ENULL and app_p(sl=NULL) == ENULL
+    assert app_p(first=1) == EARG                 # ceil(120/64) = 2
+    assert app_p(n_new=0) == EARG                 # positions 120..135 start chunk 2
+    assert app_p(n=4, n_new=1) == EARG            # 120..123 stay in chunk 1: no new chunk
+    assert app_p(ctx=640, first=10, n_new=1) == ETABLE      # past the table
+    assert app_p(n_slots=5) == ETABLE                       # slot 5 out of range
+    assert app_p(n=0) == EARG and app_p(ctx=-1) == EARG

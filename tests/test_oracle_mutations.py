@@ -111,3 +111,50 @@ def test_planted_v_transpose_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(A, "gather_paged", wrong)
     o, _ = oracle.attention_paged(c.q, c.k_pool, c.v_pool, c.page_table, 500)
     assert not (np.abs(o - ref[0]).max() <= 1e-3)   # wrong values or NaN from unset slots
+
+
+# --- the cache oracle: planted mistakes in copies of the append / commit rules --------------
+
+def _cache_mutant(kind):
+    """(append_ring, append_paged, PagerModel) with one planted mistake."""
+    from oracle import cache as C
+
+    def append_ring(k_ring, v_ring, k_new, v_new, pos_first):
+        k, v = np.array(k_ring, copy=True), np.array(v_ring, copy=True)
+        ring = k.shape[0] * C.CHUNK
+        for i in range(k_new.shape[0]):
+            s = (pos_first + i + (1 if kind == "ring_slot_shift" else 0)) % ring
+            for g in range(k_new.shape[1]):
+                k[s // C.CHUNK, g, s % C.CHUNK, :] = k_new[i, g, :]
+                if kind == "v_key_major":
+                    v[s // C.CHUNK, g, s % C.CHUNK, :] = v_new[i, g, :]
+                else:
+                    v[s // C.CHUNK, g, :, s % C.CHUNK] = v_new[i, g, :]
+        return k, v
+
+    class Pager(C.PagerModel):
+        def commit(self, n_keep):
+            if kind != "free_committed_chunk":
+                return super().commit(n_keep)
+            _, first, k = self.pending
+            self.ctx += n_keep
+            keep = self.ctx // C.CHUNK                 # floor: frees a partly committed chunk
+            for c in range(first + k - 1, first - 1, -1):
+                if c < keep:
+                    break
+                self.free.append(self.table[c])
+                self.table[c] = -1
+            self.pending = None
+
+    return append_ring, C.append_paged, Pager
+
+
+@pytest.mark.parametrize("kind", ["ring_slot_shift", "v_key_major", "free_committed_chunk"])
+def test_cache_pins_catch_planted_mistakes(kind, monkeypatch):
+    from test_oracle_cache import sequence_matches
+    assert sequence_matches(seed=1, q_len=16, ring=256, window=100, prefill=150)
+    ar, ap, P = _cache_mutant(kind)
+    monkeypatch.setattr(oracle, "append_ring", ar)
+    monkeypatch.setattr(oracle, "append_paged", ap)
+    monkeypatch.setattr(oracle, "PagerModel", P)
+    assert not sequence_matches(seed=1, q_len=16, ring=256, window=100, prefill=150)
