@@ -18,8 +18,8 @@ LIB = os.path.join(HERE, "libring_kv.so")
 # measurement-only streaming read probe, used by bench.py (not part of the C interface)
 PROBE_LIB = os.path.join(HERE, "libring_kv_probe.so")
 PROBE_SRC = "probe.hip"
-SOURCES = ["abi.hip", "attn_chunked.hip", "attn_merge.hip", "attn_contig.hip", "accept.hip",
-           "layout.hip", "pager.cpp"]
+SOURCES = ["abi.hip", "attn_chunked.hip", "attn_prefill.hip", "attn_merge.hip",
+           "attn_contig.hip", "accept.hip", "layout.hip", "pager.cpp"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms stay off: hipcc would otherwise form v_pk_* f32 ops from plain float

@@ -35,10 +35,24 @@ float scale_log2(const rkv_attn_dims* d) {
 
 int rows_of(const rkv_attn_dims* d) { return d->q_len * (d->n_q_heads / d->n_kv_heads); }
 
-// Split n_chunks whole chunks into ranges: num_splits <= 0 asks for about one workgroup per
-// compute unit across all KV heads.  Returns the split count actually used (no empty split
-// unless the caller asked for more splits than chunks) and the chunks per split.
-void choose_splits(int64_t n_chunks, int n_kv_heads, int32_t requested, int32_t* splits,
+enum Store { kContig, kRing, kPaged };
+
+// Split count the automatic choice aims at: about one workgroup per compute unit over all
+// (KV head, row tile) pairs.  A prefill block over the ring is the exception: its row tiles
+// fill the chip by themselves and each sees only a window of keys, so it is not split.
+int64_t auto_split_target(const rkv_attn_dims* d, Store store) {
+  const int rows = rows_of(d);
+  const bool prefill = store != kContig && rows > rkv::kVerifyMaxRows;
+  if (prefill && store == kRing) return 1;
+  const int tile = prefill ? rkv::kPrefillTileRows : 64;
+  const int64_t units = (int64_t)d->n_kv_heads * ((rows + tile - 1) / tile);
+  return (kTargetWorkgroups + units - 1) / units;
+}
+
+// Split n_chunks whole chunks into ranges: num_splits <= 0 asks for `target` splits.  Returns
+// the split count actually used (no empty split unless the caller asked for more splits than
+// chunks) and the chunks per split.
+void choose_splits(int64_t n_chunks, int64_t target, int32_t requested, int32_t* splits,
                    int32_t* cps) {
   if (n_chunks <= 0) { *splits = 1; *cps = 1; return; }
   if (requested > 0) {
@@ -46,7 +60,7 @@ void choose_splits(int64_t n_chunks, int n_kv_heads, int32_t requested, int32_t*
     *cps = (int32_t)((n_chunks + requested - 1) / requested);
     return;
   }
-  int64_t s = (kTargetWorkgroups + n_kv_heads - 1) / n_kv_heads;
+  int64_t s = target;
   if (s > n_chunks) s = n_chunks;
   if (s < 1) s = 1;
   const int64_t c = (n_chunks + s - 1) / s;
@@ -56,11 +70,11 @@ void choose_splits(int64_t n_chunks, int n_kv_heads, int32_t requested, int32_t*
 
 // Splits for n_chunks when the workspace was sized for n_max >= n_chunks chunks: never more
 // splits than that workspace holds.
-void split_within(int64_t n_chunks, int64_t n_max, int n_kv_heads, int32_t requested,
+void split_within(int64_t n_chunks, int64_t n_max, int64_t target, int32_t requested,
                   int32_t* splits, int32_t* cps) {
   int32_t s_max, c_max;
-  choose_splits(n_max, n_kv_heads, requested, &s_max, &c_max);
-  choose_splits(n_chunks, n_kv_heads, requested, splits, cps);
+  choose_splits(n_max, target, requested, &s_max, &c_max);
+  choose_splits(n_chunks, target, requested, splits, cps);
   if (*splits > s_max) {
     *splits = s_max;
     *cps = (int32_t)((n_chunks + s_max - 1) / s_max);
@@ -182,7 +196,7 @@ size_t decode_attn_ref_layout_workspace_bytes(const rkv_attn_dims* dims, int64_t
   int64_t c_first, n_chunks;
   contig_range(dims, ctx_len, 0, &c_first, &n_chunks);
   int32_t s, cps;
-  choose_splits(n_chunks, dims->n_kv_heads, num_splits, &s, &cps);
+  choose_splits(n_chunks, auto_split_target(dims, kContig), num_splits, &s, &cps);
   return partial_bytes(dims, s);
 }
 
@@ -199,7 +213,7 @@ int32_t decode_attn_ref_layout(const rkv_attn_dims* dims, const void* q, const v
   contig_range(dims, ctx_len, window, &c_first, &n_chunks);
   contig_range(dims, ctx_len, 0, &c0, &nfull);
   int32_t s, cps;
-  split_within(n_chunks, nfull, dims->n_kv_heads, num_splits, &s, &cps);
+  split_within(n_chunks, nfull, auto_split_target(dims, kContig), num_splits, &s, &cps);
   if (s > 1 && (workspace == nullptr || workspace_bytes < partial_bytes(dims, s)))
     return RKV_ERR_WORKSPACE;
   rkv::ContigArgs a{};
@@ -248,7 +262,8 @@ size_t verify_attn_ring_workspace_bytes(const rkv_attn_dims* dims, int32_t ring_
                                         int32_t window, int32_t num_splits) {
   if (check_dims(dims) != RKV_OK || window < 1 || num_splits < 0 || ring_size < kChunk) return 0;
   int32_t s, cps;
-  choose_splits(ring_max_chunks(dims, window), dims->n_kv_heads, num_splits, &s, &cps);
+  choose_splits(ring_max_chunks(dims, window), auto_split_target(dims, kRing), num_splits, &s,
+                &cps);
   return partial_bytes(dims, s);
 }
 
@@ -264,7 +279,8 @@ int32_t verify_attn_ring(const rkv_attn_dims* dims, const void* q, const void* k
   int64_t c_first, n_chunks;
   ring_range(dims, pos0, window, &c_first, &n_chunks);
   int32_t s, cps;
-  split_within(n_chunks, ring_max_chunks(dims, window), dims->n_kv_heads, num_splits, &s, &cps);
+  split_within(n_chunks, ring_max_chunks(dims, window), auto_split_target(dims, kRing),
+               num_splits, &s, &cps);
   if (s > 1 && (workspace == nullptr || workspace_bytes < partial_bytes(dims, s)))
     return RKV_ERR_WORKSPACE;
   ChunkAttnArgs a{};
@@ -297,7 +313,7 @@ int32_t verify_attn_paged_auto_splits(const rkv_attn_dims* dims, int64_t ctx_len
                                       int32_t chunk_size) {
   if (check_dims(dims) != RKV_OK || chunk_size != kChunk || ctx_len < 1) return 0;
   int32_t s, cps;
-  choose_splits((ctx_len + kChunk - 1) / kChunk, dims->n_kv_heads, 0, &s, &cps);
+  choose_splits((ctx_len + kChunk - 1) / kChunk, auto_split_target(dims, kPaged), 0, &s, &cps);
   return s;
 }
 
@@ -307,7 +323,8 @@ size_t verify_attn_paged_workspace_bytes(const rkv_attn_dims* dims, int64_t ctx_
       num_splits < 0)
     return 0;
   int32_t s, cps;
-  choose_splits((ctx_len + kChunk - 1) / kChunk, dims->n_kv_heads, num_splits, &s, &cps);
+  choose_splits((ctx_len + kChunk - 1) / kChunk, auto_split_target(dims, kPaged), num_splits,
+                &s, &cps);
   return partial_bytes(dims, s);
 }
 
@@ -322,7 +339,8 @@ int32_t verify_attn_paged(const rkv_attn_dims* dims, const void* q, const void* 
   if (out == nullptr) return RKV_ERR_NULL;
   if (num_splits < 0) return RKV_ERR_ARG;
   ChunkAttnArgs a = paged_args(dims, q, k_pool, v_pool, page_table, n_slots, ctx_len);
-  choose_splits(a.n_chunks, dims->n_kv_heads, num_splits, &a.num_splits, &a.cps);
+  choose_splits(a.n_chunks, auto_split_target(dims, kPaged), num_splits, &a.num_splits,
+                &a.cps);
   if (a.num_splits > 1 &&
       (workspace == nullptr || workspace_bytes < partial_bytes(dims, a.num_splits)))
     return RKV_ERR_WORKSPACE;

@@ -594,6 +594,7 @@ hipError_t launch_d(const ChunkAttnArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_chunk_attn(const ChunkAttnArgs& a, hipStream_t stream) {
+  if (a.q_len * a.G > kVerifyMaxRows) return launch_prefill_attn(a, stream);
   if (a.head_dim == 128) return launch_d<128>(a, stream);
   return launch_d<64>(a, stream);
 }

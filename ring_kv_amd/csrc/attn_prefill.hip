@@ -1,0 +1,393 @@
+// Attention of a long query block (batched prefill: hundreds to thousands of queries) over a
+// chunked KV store: the paged pool of 64-token chunks (lucebox post "Laguna XS 2.1 33B on a
+// RTX 3090: 296 tok/s peak, 152 tok/s at 256K context", "Three optimizations", item 1) and the
+// sliding-window position ring (same post, "3. Ring caches for the sliding-window layers"; its
+// "TL;DR" runs prefill as pooled batches plus ring attention).  Same arguments, definition and
+// partial format as the verify-block kernel; what differs is the balance of work.  A 16-query
+// verify block is bound by streaming the KV from HBM; a 1024-query block does 64 times the
+// arithmetic per key and is bound by the matrix cores, so the tiling favours reuse of every
+// K/V element staged in LDS:
+//
+//   workgroup = one KV head g, one split (range of whole chunks), one tile of 32*NW rows; each of
+//   its NW waves owns 32 rows and computes, per 64-key chunk,
+//     S^T [64 keys x 32 rows] = K [64 x D] . Q^T          2 x (D/16) MFMA 32x32x16 bf16
+//     online softmax of each row over the chunk's keys  (f32, exp2 domain)
+//     O^T [D x 32 rows]     += V^T [D x 64] . P^T         (D/32) x 4 MFMA 32x32x16 bf16
+//
+// S is computed transposed so that each lane ends with 16 scores of ONE row per 32-key tile,
+// which after a fixed permutation of the keys (rho below) is exactly the B operand of P^T for
+// the second product: P never goes through LDS.  Q stays in registers for the whole split.
+//
+// A workgroup only visits the chunks its rows can see (its tile's causal end and, for a window,
+// its first query's window start), so a split of the key range may leave a tile nothing to do:
+// its partial is then empty (lse -inf), which the merge gives no weight.
+#include "rkv_device.hpp"
+#include "rkv_launch.hpp"
+
+#include <type_traits>
+
+namespace rkv {
+
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// 32x32x16 bf16 MFMA: lane l supplies row (l & 31) of A and column (l & 31) of B, each as 8
+// k-values of k-group (l >> 5); C lane l holds column (l & 31), rows 8*(v/4) + 4*(l>>5) + v%4
+// for its 16 items v.
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// S^T row i of 32-key tile kt -> key within the chunk: bits 2 and 3 of i swapped.  Lane half h
+// then holds, in items 8b .. 8b+7 of tile kt, the keys 16*(2kt+b) + 8h + 0..7: for every
+// 16-key block of the PV product, the 8 consecutive keys its B operand wants from that lane.
+__device__ __forceinline__ int rho(int kt, int i) {
+  return 32 * kt + ((i & 0x13) | ((i & 4) << 1) | ((i & 8) >> 1));
+}
+
+// XOR swizzles of the 16-byte pieces of an LDS row.  A K operand read touches 32 keys rho(kt, m)
+// at one piece; the swizzle is a function of the key's low bits chosen so that every group of 8
+// lanes hits 8 distinct 16-byte slots of a 128-byte bank line and every group of 16 lanes 16
+// distinct slots of a 256-byte line.  V^T reads touch 32 consecutive dimension rows at one piece.
+template <int D>
+__device__ __forceinline__ int swz_k(int key) {
+  return D == 128 ? ((key & 3) | ((key >> 1) & 4) | ((key << 1) & 8))
+                  : (((key ^ (key >> 2)) & 1) | (key & 2) | ((key >> 1) & 4));
+}
+__device__ __forceinline__ int swz_v(int d) { return ((d >> 1) & 7) ^ ((d & 1) << 2); }
+
+constexpr float kRescaleSlack = 8.0f;   // lazy rescaling threshold (exp2 domain)
+
+__device__ __forceinline__ int rel_pos(int64_t x, int64_t base) {
+  return (int)imax64(-(int64_t(1) << 29), imin64(x - base, int64_t(1) << 29));
+}
+
+// the other lane of this lane's row (lane ^ 32) and this lane's value, combined by max / sum
+__device__ __forceinline__ float pair_max(float v) {
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+template <int D>
+struct PTile {
+  static constexpr int kRow = D / 8;            // 16-byte pieces per K row
+  static constexpr int kPieces = 64 * kRow;     // K pieces per chunk
+  static constexpr int vPieces = D * 8;         // V pieces per chunk
+  static constexpr int elems = 2 * 64 * D;      // bf16 elements per LDS tile
+  __device__ static __forceinline__ int k_off(int key, int piece) {
+    return key * D + ((piece ^ swz_k<D>(key)) << 3);
+  }
+  __device__ static __forceinline__ int v_off(int d, int piece) {
+    return 64 * D + d * 64 + ((piece ^ swz_v(d)) << 3);
+  }
+};
+
+template <int D, int NW, bool PAGED>
+__global__ __launch_bounds__(NW * 64, 2)
+void prefill_attn_kernel(ChunkAttnArgs a) {
+  using T = PTile<D>;
+  constexpr int NT = NW * 64;
+  constexpr int ROWS = 32 * NW;
+  constexpr int LPC = (T::kPieces + T::vPieces) / NT;   // 16-byte loads per chunk per thread
+  static_assert((T::kPieces + T::vPieces) % NT == 0 && T::kPieces % NT == 0, "piece split");
+  constexpr int KK = D / 16;    // 16-dim steps of S^T
+  constexpr int DT = D / 32;    // 32-dim tiles of O^T
+
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][T::elems];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31;
+  const int h = lane >> 5;
+
+  // ---- work item: (KV head, split, row tile), consecutive tiles of one (head, split) on one XCD
+  const int n_tiles = gridDim.x / (a.n_kv_heads * a.num_splits);
+  const int b = xcd_block(blockIdx.x, gridDim.x);
+  const int tile = b % n_tiles;
+  const int gs = b / n_tiles;
+  const int g = gs % a.n_kv_heads;
+  const int s = gs / a.n_kv_heads;
+  const int G = a.G;
+  const int rows = a.q_len * G;
+  const int row0 = tile * ROWS;
+
+  // ---- the chunks this tile can see within its split ----------------------------------------
+  const int64_t tq0 = row0 / G;
+  const int64_t tq1 = (int64_t)(min(row0 + ROWS, rows) - 1) / G;
+  const int64_t p_first64 = a.p0 + tq0;                      // earliest query of the tile
+  const int64_t p_last64 = a.p0 + tq1;
+  const int64_t lo_first64 = a.window > 0 ? imax64(0, p_first64 - a.window + 1) : 0;
+  const int64_t lo_last64 = a.window > 0 ? imax64(0, p_last64 - a.window + 1) : 0;
+  const int64_t s_lo = a.c_first + (int64_t)s * a.cps;
+  const int64_t s_hi = imin64(s_lo + a.cps, a.c_first + a.n_chunks);
+  const int64_t c_from = imax64(s_lo, imax64(lo_first64, a.valid_lo) / 64);
+  const int64_t c_to = imin64(s_hi, imin64(p_last64, a.valid_hi - 1) / 64 + 1);
+  const int nloc = (int)imax64(0, c_to - c_from);
+
+  // ---- this lane's row -------------------------------------------------------------------------
+  const int r = row0 + 32 * w + n;
+  const bool row_ok = r < rows;
+  const int qi = row_ok ? r / G : 0;
+  const int hq = g * G + (row_ok ? r % G : 0);
+  const int64_t pbase = c_from * 64;
+  const int64_t p_i64 = a.p0 + qi;
+  const int p_i = rel_pos(p_i64, pbase);
+  const int lo_i = rel_pos(a.window > 0 ? imax64(0, p_i64 - a.window + 1) : 0, pbase);
+  const int vlo = rel_pos(a.valid_lo, pbase);
+  const int vhi = rel_pos(a.valid_hi, pbase);
+
+  // ---- slots ------------------------------------------------------------------------------------
+  constexpr bool paged = PAGED;
+  const int ring_base = paged ? 0 : (int)(c_from % a.n_slots);
+  // the slot of local chunk loc (loc < nloc), or -1 when the table points outside the pool
+  auto slot_at = [&](int loc) __attribute__((always_inline)) -> int {
+    if (!paged) {
+      int t = ring_base + loc % a.n_slots;
+      return t >= a.n_slots ? t - a.n_slots : t;
+    }
+    const int v = __builtin_amdgcn_readfirstlane(a.pt[c_from + loc]);
+    return (unsigned)v < (unsigned)a.n_slots ? v : -1;
+  };
+  // every table entry of the range in the pool?  (else every chunk takes the masking path)
+  bool table_ok = true;
+  if (paged) {
+    bool bad = false;
+    for (int e = tid; e < nloc; e += NT) bad |= (unsigned)a.pt[c_from + e] >= (unsigned)a.n_slots;
+    table_ok = !__syncthreads_or(bad);
+  }
+
+  // ---- register stage: chunk loads, 1 KiB of contiguous HBM per wave instruction -------------
+  u32x4 stg[LPC];
+  auto issue = [&](int slot) __attribute__((always_inline)) {
+    const int sl = slot >= 0 ? slot : 0;                       // no slot: filler, never used
+    const int64_t blk = (int64_t)sl * a.n_kv_heads + g;
+    const uint16_t* kb = a.k + blk * (64 * D);
+    const uint16_t* vb = a.v + blk * (64 * D);
+#pragma unroll
+    for (int u = 0; u < LPC; ++u) {
+      const int P = u * NT + tid;
+      const uint16_t* src = (u * NT < T::kPieces) ? kb + P * 8 : vb + (P - T::kPieces) * 8;
+      stg[u] = *reinterpret_cast<const u32x4*>(src);
+    }
+  };
+  auto commit = [&](uint16_t* buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < LPC; ++u) {
+      const int P = u * NT + tid;
+      int off;
+      if (u * NT < T::kPieces) {
+        off = T::k_off(P / T::kRow, P % T::kRow);
+      } else {
+        const int vp = P - T::kPieces;
+        off = T::v_off(vp >> 3, vp & 7);
+      }
+      *reinterpret_cast<u32x4*>(buf + off) = stg[u];
+    }
+  };
+
+  // ---- Q^T operand: lane (n, h) holds row n's dims 16kk + 8h .. +7 -------------------------------
+  bf16x8 qop[KK];
+  {
+    const uint16_t* qrow = a.q + ((int64_t)qi * a.n_q_heads + hq) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + kk * 16 + h * 8);
+      if (!row_ok) raw = u32x4{0u, 0u, 0u, 0u};
+      qop[kk] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+
+  // ---- running state: m_run (exp2 domain, shared by the row's two lanes), this lane's share of
+  // the row sum, O^T accumulators -------------------------------------------------------------
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) oacc[t][v] = 0.f;
+  const float csc = a.scale_log2;
+
+  auto compute = [&](const uint16_t* buf, int loc, bool ok, auto edge_tag) __attribute__((always_inline)) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
+    const int cbase = loc * 64;
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sacc[kt][v] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const bf16x8 ka =
+            *reinterpret_cast<const bf16x8*>(buf + T::k_off(rho(kt, n), 2 * kk + h));
+        sacc[kt] = mfma_32x32x16(ka, qop[kk], sacc[kt]);
+      }
+    }
+    // item v of tile kt is key 32kt + 16(v/8) + 8h + v%8 of the chunk
+    float mx = -INFINITY;
+    if constexpr (EDGE) {
+      const int vis_lo = max(-1, min(max(lo_i, vlo) - cbase, 64));
+      const int vis_hi = (row_ok && ok) ? max(-1, min(min(p_i, vhi - 1) - cbase, 64)) : -1;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = 32 * kt + 16 * (v >> 3) + 8 * h + (v & 7);
+          if (key < vis_lo || key > vis_hi) sacc[kt][v] = -INFINITY;   // select, not arithmetic
+          mx = fmaxf(mx, sacc[kt][v]);
+        }
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) mx = fmaxf(mx, fmaxf(sacc[kt][v], sacc[kt][v + 1]));
+    }
+    const float t_max = pair_max(mx) * csc;
+    const bool grow = t_max > m_run + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? t_max : m_run;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (EDGE && m_run == -INFINITY) ? 0.f : m_run;
+    // P^T operand of 16-key block kb = 2kt + hb: items 8hb .. 8hb+7 of tile kt
+    bf16x8 pb[4];
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      uint32_t wds[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb >> 1][8 * (kb & 1) + 2 * e], csc, -m_use));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb >> 1][8 * (kb & 1) + 2 * e + 1], csc, -m_use));
+        lsum += p0 + p1;
+        wds[e] = pack_bf16x2(p0, p1);
+      }
+      pb[kb] = __builtin_bit_cast(bf16x8, u32x4{wds[0], wds[1], wds[2], wds[3]});
+    }
+    l_run += lsum;
+    // keys outside the stored range or without a slot: zero their V, so 0 * (anything) = 0
+    uint32_t vmask[4][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vmask[kb][e] = 0xffffffffu;
+    if constexpr (EDGE) {
+      if (!ok || cbase < vlo || cbase + 64 > vhi) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int jj = cbase + 16 * kb + 8 * h + e;
+            if (!ok || jj < vlo || jj >= vhi) vmask[kb][e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+          }
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        u32x4 raw = *reinterpret_cast<const u32x4*>(buf + T::v_off(32 * t + n, 2 * kb + h));
+        if constexpr (EDGE) {
+          raw[0] &= vmask[kb][0]; raw[1] &= vmask[kb][1];
+          raw[2] &= vmask[kb][2]; raw[3] &= vmask[kb][3];
+        }
+        oacc[t] = mfma_32x32x16(__builtin_bit_cast(bf16x8, raw), pb[kb], oacc[t]);
+      }
+    }
+  };
+
+  // ---- pipeline: chunk loc + 1 in registers while chunk loc is computed ------------------------
+  // Step loc: barrier (every wave is done with chunk loc - 1, and chunk loc's tile is written);
+  // write chunk loc + 1 from the stage into the other tile; load chunk loc + 2 into the stage;
+  // compute chunk loc.  Loads past the range read slot 0 and are never computed.
+  if (nloc > 0) {
+    int sl_cur = slot_at(0);
+    int sl_nxt = nloc > 1 ? slot_at(1) : -1;
+    int sl_far = nloc > 2 ? slot_at(2) : -1;
+    issue(sl_cur);
+    commit(&lds[0][0]);
+    issue(sl_nxt);
+
+    auto step = [&](int loc, auto edge_tag) __attribute__((always_inline)) {
+      lds_barrier();
+      commit(&lds[(loc + 1) & 1][0]);
+      issue(sl_far);
+      const int sl_more = loc + 3 < nloc ? slot_at(loc + 3) : -1;
+      compute(&lds[loc & 1][0], loc, sl_cur >= 0, edge_tag);
+      sl_cur = sl_nxt;
+      sl_nxt = sl_far;
+      sl_far = sl_more;
+    };
+    // interior chunks [ca, cb): after every row's window start and the stored range's start,
+    // ending at or before the tile's first query and the stored range's end
+    int ca = nloc, cb = nloc;
+    if (table_ok) {
+      const int lead = max(max(rel_pos(lo_last64, pbase), vlo), 0);
+      ca = min((lead + 63) / 64, nloc);
+      const int end = max(min(rel_pos(p_first64, pbase) + 1, vhi), 0) / 64;
+      cb = max(ca, min(end, nloc));
+    }
+    int loc = 0;
+    for (; loc < ca; ++loc) step(loc, std::true_type{});
+    for (; loc < cb; ++loc) step(loc, std::false_type{});
+    for (; loc < nloc; ++loc) step(loc, std::true_type{});
+  }
+
+  // ---- epilogue ---------------------------------------------------------------------------------
+  if (!row_ok) return;
+  const float l = pair_sum(l_run);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float lse_nat = l > 0.f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+  float* dst;
+  if (a.part_o == nullptr) {
+    dst = a.out + ((int64_t)qi * a.n_q_heads + hq) * D;
+    if (a.lse != nullptr && h == 0) a.lse[(int64_t)qi * a.n_q_heads + hq] = lse_nat;
+  } else {
+    const int64_t prow = ((int64_t)g * a.num_splits + s) * rows + r;
+    dst = a.part_o + prow * D;
+    if (h == 0) a.part_lse[prow] = lse_nat;
+  }
+  // item v of dim tile t is dimension 32t + 8(v/4) + 4h + v%4
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 o = f32x4{oacc[t][4 * j], oacc[t][4 * j + 1], oacc[t][4 * j + 2],
+                            oacc[t][4 * j + 3]} * inv;
+      *reinterpret_cast<f32x4*>(dst + 32 * t + 8 * j + 4 * h) = o;
+    }
+}
+
+template <int D>
+hipError_t launch_d(const ChunkAttnArgs& a, hipStream_t stream) {
+  constexpr int NW = kPrefillTileRows / 32;
+  const int rows = a.q_len * a.G;
+  const int tiles = (rows + kPrefillTileRows - 1) / kPrefillTileRows;
+  const dim3 blocks(a.n_kv_heads * a.num_splits * tiles);
+  if (a.pt != nullptr)
+    hipLaunchKernelGGL((prefill_attn_kernel<D, NW, true>), blocks, dim3(NW * 64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((prefill_attn_kernel<D, NW, false>), blocks, dim3(NW * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_attn(const ChunkAttnArgs& a, hipStream_t stream) {
+  if (a.head_dim == 128) return launch_d<128>(a, stream);
+  return launch_d<64>(a, stream);
+}
+
+}  // namespace rkv

@@ -34,7 +34,13 @@ struct ChunkAttnArgs {
   float* part_o;          // otherwise partials [Hkv][S][rows][D]
   float* part_lse;        //                    and [Hkv][S][rows]
 };
+// Blocks of up to kVerifyMaxRows rows per KV head (a verify block: q_len * G) run the
+// HBM-streaming kernel with 64-row tiles; longer blocks (batched prefill) run the matrix-core
+// kernel with tiles of kPrefillTileRows rows.  launch_chunk_attn picks the kernel.
+constexpr int kVerifyMaxRows = 256;
+constexpr int kPrefillTileRows = 256;
 hipError_t launch_chunk_attn(const ChunkAttnArgs& a, hipStream_t stream);
+hipError_t launch_prefill_attn(const ChunkAttnArgs& a, hipStream_t stream);
 
 struct MergeArgs {
   const float* part_o;

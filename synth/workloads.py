@@ -12,6 +12,14 @@ Named workloads (sizes in the names):
 * ``stack_40l_131k``  - 40 layers: ``l % 4 != 3`` ring layers (block at 131,056), else paged
   layers at context 131,072 (2,048 permuted chunks); accept over [17 x 65536] logits with an
   argmax margin of at least 1e-3 and an agreement prefix ~ Binomial(16, 9/16).
+
+Batched prefill (1,024-token blocks through the same stores, 16 / 4 heads, head_dim 128, bf16):
+
+* ``prefill_pool_8k``   - block after 8,192 prior tokens (context 9,216), 144 permuted chunks.
+* ``prefill_ring_w512`` - block at absolute position 30,000 over the wrapped 2,048-slot ring,
+  window 512.
+* ``prefill_pool_131k`` - block ending at context 131,072 (2,048 permuted chunks): the paged
+  layers of the 40-layer stack, one prefill block further on.
 """
 from __future__ import annotations
 
@@ -33,7 +41,7 @@ __all__ = [
 #: seed ids of the named workloads
 WORKLOAD_IDS = {
     "contig_1k_f32": 1, "ring_w512_r2048": 2, "paged_8k": 3, "paged_256k": 4,
-    "stack_40l_131k": 5,
+    "stack_40l_131k": 5, "prefill_pool_8k": 6, "prefill_ring_w512": 7, "prefill_pool_131k": 8,
 }
 STACK_LAYERS = 40
 
@@ -202,4 +210,11 @@ def workload(name: str, layer: int = 0, keep_rows: bool = True):
         else:
             a = paged_case(wid, layer, 131072, 16, 16, 4, 128, n_slots=2048, keep_rows=keep_rows)
         return a, accept_case(wid, 0, 16, 65536, 1e-3, "binomial")
+    if name == "prefill_pool_8k":
+        return paged_case(wid, 0, 9216, 1024, 16, 4, 128, keep_rows=keep_rows), None
+    if name == "prefill_ring_w512":
+        return ring_case(wid, 0, 30000, 1024, 16, 4, 128, 2048, 512, keep_rows=keep_rows), None
+    if name == "prefill_pool_131k":
+        return paged_case(wid, 0, 131072, 1024, 16, 4, 128, n_slots=2048,
+                          keep_rows=keep_rows), None
     raise KeyError(name)

@@ -42,7 +42,7 @@ def test_paged_argument_checks():
     assert paged(q=NULL) == ENULL and paged(pt=NULL) == ENULL and paged(out=NULL) == ENULL
     assert paged(d=dims(d=96)) == ESHAPE
     assert paged(d=dims(hq=10, hkv=4)) == ESHAPE
-    assert paged(d=dims(q_len=65)) == ESHAPE            # 65 * 4 rows > 256
+    assert paged(d=dims(q_len=4097)) == ESHAPE          # 4097 * 4 rows > 16384
     assert paged(d=dims(q_len=0)) == ESHAPE
     assert paged(d=dims(dtype=0)) == EDTYPE               # the chunked stores are bf16
     assert paged(d=dims(dtype=7)) == EDTYPE
@@ -75,6 +75,24 @@ def test_paged_workspace_and_splits():
     assert L.verify_attn_paged_auto_splits(d, 131072, 64) == 64
     assert L.verify_attn_paged_auto_splits(d, 65, 64) == 2
     assert L.verify_attn_paged_workspace_bytes(d, 262144, 32, 0) == 0    # unsupported chunk
+
+
+def test_prefill_block_splits():
+    # a 1024-token block (4096 rows per KV head) runs 256-row tiles over the pool: 4 heads x 16
+    # tiles, so 4 splits give one workgroup per compute unit; partials [4][4][4096][128] f32
+    d = dims(q_len=1024)
+    assert L.verify_attn_paged_auto_splits(d, 9216, 64) == 4
+    want = 4 * 4 * 4096 * 128 * 4 + 4 * 4 * 4096 * 4
+    assert L.verify_attn_paged_workspace_bytes(d, 9216, 64, 0) == want
+    assert L.verify_attn_paged_auto_splits(d, 131072, 64) == 4
+    # over the ring the block is not split: no partials
+    assert L.verify_attn_ring_workspace_bytes(d, 2048, 512, 0) == 0
+    assert L.verify_attn_ring_workspace_bytes(d, 1024, 512, 0) == 0
+    # 17..64-query verify blocks: 2..4 row tiles of 64 share the chip
+    assert L.verify_attn_paged_auto_splits(dims(q_len=32), 262144, 64) == 32
+    # the longest block one call takes
+    assert L.verify_attn_paged_auto_splits(dims(q_len=4096), 262144, 64) == 1
+    assert L.verify_attn_paged_auto_splits(dims(q_len=4097), 262144, 64) == 0
 
 
 def ring(d=None, pos0=30000, head=1328, size=2048, window=512, splits=0, ws=P, wsb=1 << 30):
