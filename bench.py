@@ -9,7 +9,8 @@ data already resident in HBM; the step is captured once in a HIP graph and repla
 
 The JSON line also carries the per-layer figure at context 262,144 (one paged verify layer,
 both kernels), the roofline of the dominant kernel (the paged split-K attention kernel, timed
-live with HIP events on the stream it runs on), the step by layer type, the four single-layer
+live with HIP events on the stream it runs on), the step by layer type, 1,024-token prefill
+blocks through the pool and the ring (with their own matrix-core roofline), the four single-layer
 workloads timed one by one (cold and warm, median / p10 / p90), a measured HBM read bandwidth,
 and the fp64 oracle timed on the host cores over a bounded sample of the same workload (plus one
 call per single-layer workload).
@@ -18,8 +19,8 @@ call per single-layer workload).
     python bench.py --mode copy     # plain 1-GiB device copies, for HBM counter calibration
     python bench.py --mode kernel   # the dominant kernel alone (10 launches), for counter runs
     python bench.py --mode configs  # each single-layer workload and block append called 100
-                                    # times (30 at 256K), a cache-evicting read before each,
-                                    # for a kernel trace
+                                    # times (30 at 256K and for the prefill blocks), a
+                                    # cache-evicting read before each, for a kernel trace
     python bench.py --mode traffic --fetch F.csv --write W.csv --copy-fetch CF.csv --copy-write CW.csv
                                     # HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE /
                                     # WRITE_SIZE counter files, scaled by the copy calibration
@@ -62,6 +63,8 @@ def parse():
     ap.add_argument("--no-256k", action="store_true", help="skip the 262,144-context layer")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the single-layer workloads timed one by one")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the 1,024-token prefill blocks")
     return ap.parse_args()
 
 
@@ -351,6 +354,85 @@ def config_calls(torch, rk, synth, probe, n_small, n_large):
     vp = torch.zeros((2048, 4, 128, 64), dtype=torch.bfloat16, device="cuda")
     table = torch.arange(2050, dtype=torch.int32, device="cuda") % 2048
     run(lambda: rk.verify_kv_append_paged(kb, kb, 131064, kp, vp, table, 2048, [2047]), n_small)
+    del kp, vp
+    torch.cuda.empty_cache()
+    # 1,024-token prefill blocks through the pool and the ring
+    for name in ("prefill_pool_8k", "prefill_ring_w512", "prefill_pool_131k"):
+        c, _ = synth.workload(name, keep_rows=False)
+        q = t(c.q)
+        o, l = f32(c.q_len, 16, 128), f32(c.q_len, 16)
+        if c.kind == "ring":
+            kr, vr = t(c.k_ring), t(c.v_ring)
+            run(lambda: rk.verify_attn_ring(q, kr, vr, c.pos0, c.window, out=o, lse=l), n_large)
+        else:
+            kp, vp, pt = t(c.k_pool), t(c.v_pool), t(c.page_table)
+            run(lambda: rk.verify_attn_paged(q, kp, vp, pt, c.ctx_len, out=o, lse=l), n_large)
+            del kp, vp
+        torch.cuda.empty_cache()
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, vendor figure
+
+
+def prefill_timings(torch, rk, synth, reps):
+    """Batched prefill: 1,024-token blocks through the pool (after 8,192 and 130,048 prior
+    tokens) and the ring (window 512), each call captured in a HIP graph and replayed (mean µs
+    per call; the calls are bound by the matrix cores, so warm and cold agree).  Also the paged
+    split kernel alone at 131,072 (the prefill roofline: flops of the keys each query sees over
+    its launch time) and the attention of one prefill block through the 40-layer stack."""
+    import ctypes
+    from ring_kv_amd._lib import AttnDims
+    t = lambda a: rk.tensor_from_numpy(a, "cuda")  # noqa: E731
+    out = {}
+    for name in ("prefill_pool_8k", "prefill_ring_w512", "prefill_pool_131k"):
+        c, _ = synth.workload(name, keep_rows=False)
+        q = t(c.q)
+        o = torch.empty((c.q_len, c.n_q_heads, c.head_dim), dtype=torch.float32, device="cuda")
+        l = torch.empty((c.q_len, c.n_q_heads), dtype=torch.float32, device="cuda")
+        flops = attn_flops(c)
+        e = {"q_len": c.q_len, "flops": flops}
+        if c.kind == "ring":
+            kr, vr = t(c.k_ring), t(c.v_ring)
+            fn = lambda: rk.verify_attn_ring(q, kr, vr, c.pos0, c.window, out=o, lse=l)  # noqa: E731
+            e["splits"] = 1
+        else:
+            kp, vp, pt = t(c.k_pool), t(c.v_pool), t(c.page_table)
+            S = rk.verify_attn_paged_auto_splits(16, 4, 128, c.q_len, c.ctx_len)
+            ws = torch.empty(rk.lib().verify_attn_paged_workspace_bytes(
+                ctypes.byref(AttnDims(c.q_len, 16, 4, 128, 0.0, 1)), c.ctx_len, 64, 0),
+                dtype=torch.uint8, device="cuda")
+            fn = lambda: rk.verify_attn_paged(q, kp, vp, pt, c.ctx_len, out=o, lse=l,  # noqa: E731
+                                              workspace=ws)
+            e["splits"] = S
+            if name == "prefill_pool_131k":
+                rows = c.q_len * 4
+                po = torch.empty((4, S, rows, 128), dtype=torch.float32, device="cuda")
+                pl = torch.empty((4, S, rows), dtype=torch.float32, device="cuda")
+                part = lambda: rk.verify_attn_paged_partial(q, kp, vp, pt, c.ctx_len, S,  # noqa: E731
+                                                            part_out=po, part_lse=pl)
+                k_us = graph_ms(part, 2, reps, torch) * 1e3
+                tf = flops / (k_us * 1e-6) / 1e12
+                out["roofline_mfma"] = {
+                    "bound": "mfma",
+                    "kernel": "prefill_attn_kernel (paged, 256-row tiles, 4 splits) at 131,072",
+                    "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "us_per_launch": round(k_us, 1),
+                    "algorithmic_flops_per_launch": flops, "traffic": None}
+        us = graph_ms(fn, 2, reps, torch) * 1e3
+        tf = flops / (us * 1e-6) / 1e12
+        e.update({"us": round(us, 1), "tflops": round(tf, 1),
+                  "util_mfma_bf16": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                  "tokens_per_s_one_layer": round(c.q_len / (us * 1e-6))})
+        out[name] = e
+        del c
+        torch.cuda.empty_cache()
+    ring_us, pool_us = out["prefill_ring_w512"]["us"], out["prefill_pool_131k"]["us"]
+    stack_us = 30 * ring_us + 10 * pool_us
+    out["stack_40l_131k_block_attention"] = {
+        "us": round(stack_us, 1), "tokens_per_s": round(1024 / (stack_us * 1e-6)),
+        "note": "attention only (30 ring layers + 10 paged layers at 131,072) of one 1,024-token "
+                "prefill block; the pages' ~3,500 tok/s is whole-engine prefill on an RTX 3090"}
+    return out
 
 
 def read_bw_probe(torch, probe):
@@ -683,6 +765,10 @@ def main():
                                      "algorithmic_bytes_per_launch": kv, "traffic": None}})
         del q, pt, pools
         torch.cuda.empty_cache()
+
+    if not args.no_prefill:
+        log("batched prefill blocks")
+        res["prefill_gpu"] = prefill_timings(torch, rk, synth, max(3, args.steps // 4))
 
     if not args.no_configs:
         log("single-layer workloads, cold and warm")

@@ -8,9 +8,10 @@
 namespace rkv {
 namespace {
 
-// One workgroup of 256 threads per (KV head, row).  Thread (sg, d4) owns four consecutive
-// output dimensions and the splits sg, sg + SG, ...; its first kPre partial vectors are
-// requested before anything else so that the whole merge costs about one memory round trip.
+// Few rows, many splits (a verify block over a long context): one workgroup of 256 threads per
+// (KV head, row).  Thread (sg, d4) owns four consecutive output dimensions and the splits sg,
+// sg + SG, ...; its first kPre partial vectors are requested before anything else so that the
+// whole merge costs about one memory round trip.
 // The max over the splits' lse values is reduced through LDS, then every thread weighs its
 // splits, and the SG split groups are summed through LDS.
 constexpr int kMergeThreads = 256;
@@ -90,10 +91,60 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
     a.lse[(int64_t)qi * a.n_q_heads + h] = Lt > 0.f ? M + logf(Lt) : -INFINITY;
 }
 
+// Many rows, few splits (a prefill block): D/4 threads per row, each owning four consecutive
+// dimensions and walking the splits in order; no LDS, no barrier, and each row's partials are
+// read as whole 4*D-byte lines.
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void merge_rows_kernel(MergeArgs a) {
+  constexpr int TPR = D / 4;
+  constexpr int RPB = kMergeThreads / TPR;
+  const int rows = a.q_len * a.G;
+  const int64_t gr = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  if (gr >= (int64_t)a.n_kv_heads * rows) return;
+  const int g = (int)(gr / rows);
+  const int r = (int)(gr % rows);
+  const int d4 = (threadIdx.x % TPR) * 4;
+  const int S = a.num_splits;
+  const float* lse = a.part_lse + (int64_t)g * S * rows + r;
+  const float* po = a.part_o + ((int64_t)g * S * rows + r) * D + d4;
+  const int64_t ostride = (int64_t)rows * D;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, lse[(int64_t)s * rows]);
+  const float Mu = M == -INFINITY ? 0.f : M;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float ls = lse[(int64_t)s * rows];
+    const float w = ls > -INFINITY ? expf(ls - Mu) : 0.f;
+    acc += *reinterpret_cast<const f32x4*>(po + s * ostride) * w;
+    L += w;
+  }
+  const int qi = r / a.G;
+  const int h = g * a.G + r % a.G;
+  *reinterpret_cast<f32x4*>(a.out + ((int64_t)qi * a.n_q_heads + h) * D + d4) =
+      L > 0.f ? acc * (1.f / L) : f32x4{0.f, 0.f, 0.f, 0.f};
+  if (a.lse != nullptr && d4 == 0)
+    a.lse[(int64_t)qi * a.n_q_heads + h] = L > 0.f ? M + logf(L) : -INFINITY;
+}
+
+// rows of all KV heads from which the row-parallel form is used (with at most kRowsMaxSplits)
+constexpr int64_t kRowsMinRows = 1024;
+constexpr int kRowsMaxSplits = 32;
+
 }  // namespace
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
-  const int blocks = a.n_kv_heads * a.q_len * a.G;
+  const int64_t all_rows = (int64_t)a.n_kv_heads * a.q_len * a.G;
+  if (all_rows >= kRowsMinRows && a.num_splits <= kRowsMaxSplits) {
+    const int rpb = kMergeThreads / (a.head_dim / 4);
+    const dim3 blocks((unsigned)((all_rows + rpb - 1) / rpb));
+    if (a.head_dim == 128)
+      hipLaunchKernelGGL(merge_rows_kernel<128>, blocks, dim3(kMergeThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL(merge_rows_kernel<64>, blocks, dim3(kMergeThreads), 0, stream, a);
+    return hipGetLastError();
+  }
+  const int blocks = (int)all_rows;
   if (a.head_dim == 128)
     hipLaunchKernelGGL(merge_kernel<128>, dim3(blocks), dim3(kMergeThreads), 0, stream, a);
   else

@@ -31,6 +31,8 @@ namespace rkv {
 namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 // 32x32x16 bf16 MFMA: lane l supplies row (l & 31) of A and column (l & 31) of B, each as 8
 // k-values of k-group (l >> 5); C lane l holds column (l & 31), rows 8*(v/4) + 4*(l>>5) + v%4
@@ -57,7 +59,11 @@ __device__ __forceinline__ int swz_k(int key) {
 }
 __device__ __forceinline__ int swz_v(int d) { return ((d >> 1) & 7) ^ ((d & 1) << 2); }
 
-constexpr float kRescaleSlack = 8.0f;   // lazy rescaling threshold (exp2 domain)
+// Lazy rescaling: a row keeps its reference max while its weights stay below 2^8, so the
+// accumulators are rescaled only rarely; a row without a reference yet keeps 0 as long as its
+// weights stay above 2^-8 (well inside f32 and bf16 range).
+constexpr float kSlackHi = 256.0f;
+constexpr float kSlackLo = 1.0f / 256.0f;
 
 __device__ __forceinline__ int rel_pos(int64_t x, int64_t base) {
   return (int)imax64(-(int64_t(1) << 29), imin64(x - base, int64_t(1) << 29));
@@ -145,13 +151,23 @@ void prefill_attn_kernel(ChunkAttnArgs a) {
   // ---- slots ------------------------------------------------------------------------------------
   constexpr bool paged = PAGED;
   const int ring_base = paged ? 0 : (int)(c_from % a.n_slots);
-  // the slot of local chunk loc (loc < nloc), or -1 when the table points outside the pool
-  auto slot_at = [&](int loc) __attribute__((always_inline)) -> int {
+  // The slot of local chunk loc (loc < nloc), or -1 when the table points outside the pool, in
+  // two halves: fetch() starts the read, slot() turns its result into the slot.  The table is
+  // read with a vector load (through an offset the compiler cannot see to be uniform) one step
+  // before the slot is needed: a scalar load would share its wait counter with the LDS reads
+  // and stall the first of them in every step.
+  int vzero;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(vzero));
+  auto fetch = [&](int loc) __attribute__((always_inline)) -> int {
+    if (!paged) return loc;
+    return a.pt[c_from + min(loc, nloc - 1) + vzero];
+  };
+  auto slot = [&](int fetched) __attribute__((always_inline)) -> int {
     if (!paged) {
-      int t = ring_base + loc % a.n_slots;
+      int t = ring_base + fetched % a.n_slots;
       return t >= a.n_slots ? t - a.n_slots : t;
     }
-    const int v = __builtin_amdgcn_readfirstlane(a.pt[c_from + loc]);
+    const int v = __builtin_amdgcn_readfirstlane(fetched);
     return (unsigned)v < (unsigned)a.n_slots ? v : -1;
   };
   // every table entry of the range in the pool?  (else every chunk takes the masking path)
@@ -203,10 +219,11 @@ void prefill_attn_kernel(ChunkAttnArgs a) {
     }
   }
 
-  // ---- running state: m_run (exp2 domain, shared by the row's two lanes), this lane's share of
-  // the row sum, O^T accumulators -------------------------------------------------------------
+  // ---- running state: m_run (exp2 domain, shared by the row's two lanes), this lane's shares of
+  // the row sums, O^T accumulators ------------------------------------------------------------
   float m_run = -INFINITY;
-  float l_run = 0.f;
+  float l_run = 0.f;      // sum of the f32 weights
+  float l_rnd = 0.f;      // sum of the same weights rounded to bf16
   f32x16 oacc[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t)
@@ -214,97 +231,117 @@ void prefill_attn_kernel(ChunkAttnArgs a) {
     for (int v = 0; v < 16; ++v) oacc[t][v] = 0.f;
   const float csc = a.scale_log2;
 
+  // Per chunk: S^T of both 32-key tiles first, then tile by tile the softmax and its half of
+  // the PV product.  The order lets the matrix core run tile 1's QK products while the vector
+  // unit works on tile 0's scores, and tile 0's PV products while it works on tile 1's.
   auto compute = [&](const uint16_t* buf, int loc, bool ok, auto edge_tag) __attribute__((always_inline)) {
     constexpr bool EDGE = decltype(edge_tag)::value;
     const int cbase = loc * 64;
     f32x16 sacc[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) sacc[kt][v] = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int kk = 0; kk < KK; ++kk) {
         const bf16x8 ka =
             *reinterpret_cast<const bf16x8*>(buf + T::k_off(rho(kt, n), 2 * kk + h));
         sacc[kt] = mfma_32x32x16(ka, qop[kk], sacc[kt]);
       }
     }
-    // item v of tile kt is key 32kt + 16(v/8) + 8h + v%8 of the chunk
-    float mx = -INFINITY;
+    // visible keys of this row relative to the chunk, and the V words of keys without a stored
+    // row or slot (zeroed, so that 0 * (anything) = 0)
+    int vis_lo = 0, vis_hi = 63;
+    bool vzero = false;
     if constexpr (EDGE) {
-      const int vis_lo = max(-1, min(max(lo_i, vlo) - cbase, 64));
-      const int vis_hi = (row_ok && ok) ? max(-1, min(min(p_i, vhi - 1) - cbase, 64)) : -1;
+      vis_lo = max(-1, min(max(lo_i, vlo) - cbase, 64));
+      vis_hi = (row_ok && ok) ? max(-1, min(min(p_i, vhi - 1) - cbase, 64)) : -1;
+      vzero = !ok || cbase < vlo || cbase + 64 > vhi;
+    }
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt) {
+      // item v of tile kt is key 32kt + 16(v/8) + 8h + v%8 of the chunk
+      if constexpr (EDGE) {
+        // key - 8h is a compile-time constant per item: compare it with the bounds shifted by 8h
+        const int lo8 = vis_lo - 8 * h, hi8 = vis_hi - 8 * h;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int key = 32 * kt + 16 * (v >> 3) + 8 * h + (v & 7);
-          if (key < vis_lo || key > vis_hi) sacc[kt][v] = -INFINITY;   // select, not arithmetic
-          mx = fmaxf(mx, sacc[kt][v]);
+          const int kc = 32 * kt + 16 * (v >> 3) + (v & 7);
+          if (kc < lo8 || kc > hi8) sacc[kt][v] = -INFINITY;   // select, not arithmetic
         }
-    } else {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int v = 0; v < 16; v += 2) mx = fmaxf(mx, fmaxf(sacc[kt][v], sacc[kt][v + 1]));
-    }
-    const float t_max = pair_max(mx) * csc;
-    const bool grow = t_max > m_run + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float m_new = grow ? t_max : m_run;
-      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-#pragma unroll
-      for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
-    }
-    const float m_use = (EDGE && m_run == -INFINITY) ? 0.f : m_run;
-    // P^T operand of 16-key block kb = 2kt + hb: items 8hb .. 8hb+7 of tile kt
-    bf16x8 pb[4];
-    float lsum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      uint32_t wds[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb >> 1][8 * (kb & 1) + 2 * e], csc, -m_use));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb >> 1][8 * (kb & 1) + 2 * e + 1], csc, -m_use));
-        lsum += p0 + p1;
-        wds[e] = pack_bf16x2(p0, p1);
       }
-      pb[kb] = __builtin_bit_cast(bf16x8, u32x4{wds[0], wds[1], wds[2], wds[3]});
-    }
-    l_run += lsum;
-    // keys outside the stored range or without a slot: zero their V, so 0 * (anything) = 0
-    uint32_t vmask[4][4];
+      // Weights against the row's current reference m_use (0 before the row has one); the max
+      // is taken over the weights, which the compiler knows are never NaN, rather than over the
+      // raw scores.  A row whose weights leave [2^-S, 2^S] while it has no reference yet, or
+      // pass 2^S, takes the rare path: reference = the tile's true max, accumulators rescaled,
+      // weights recomputed.
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
+      float pv[16];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+      for (int v = 0; v < 16; ++v) pv[v] = __builtin_amdgcn_exp2f(fmaf(sacc[kt][v], csc, -m_use));
+      float pm = pv[0];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) vmask[kb][e] = 0xffffffffu;
-    if constexpr (EDGE) {
-      if (!ok || cbase < vlo || cbase + 64 > vhi) {
+      for (int v = 1; v < 16; ++v) pm = fmaxf(pm, pv[v]);
+      pm = pair_max(pm);
+      const bool grow = pm > kSlackHi || (m_run == -INFINITY && pm < kSlackLo);
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        // the empty volatile asm keeps the compiler from executing this path unconditionally
+        asm volatile("" ::);
+        float mx = sacc[kt][0];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sacc[kt][v]);
+        const float t_max = pair_max(mx) * csc;
+        const float m_new = (grow && t_max != -INFINITY) ? t_max : m_use;
+        const float alpha = (grow && m_run != -INFINITY) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int jj = cbase + 16 * kb + 8 * h + e;
-            if (!ok || jj < vlo || jj >= vhi) vmask[kb][e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-          }
+        for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
+        l_run *= alpha;
+        l_rnd *= alpha;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) pv[v] = __builtin_amdgcn_exp2f(fmaf(sacc[kt][v], csc, -m_new));
+        m_run = (grow && t_max == -INFINITY) ? m_run : m_new;
+      } else {
+        m_run = m_use;
       }
-    }
+      // P^T operand of 16-key block kb = 2kt + hb: items 8hb .. 8hb+7 of the tile.  Two row sums:
+      // of the f32 weights (for the lse) and of the bf16 weights the PV product multiplies (to
+      // normalise the output, so that a row dominated by one key gets exactly that key's V)
+      float lsum = 0.f, lsum_r = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+      for (int hb = 0; hb < 2; ++hb) {
+        uint32_t wds[4];
 #pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        u32x4 raw = *reinterpret_cast<const u32x4*>(buf + T::v_off(32 * t + n, 2 * kb + h));
+        for (int e = 0; e < 4; ++e) {
+          wds[e] = pack_bf16x2(pv[8 * hb + 2 * e], pv[8 * hb + 2 * e + 1]);
+          lsum += pv[8 * hb + 2 * e] + pv[8 * hb + 2 * e + 1];
+          lsum_r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wds[e]), kOnes2,
+                                                   lsum_r, false);
+        }
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{wds[0], wds[1], wds[2], wds[3]});
+        const int kb = 2 * kt + hb;
+        uint32_t vmask[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
         if constexpr (EDGE) {
-          raw[0] &= vmask[kb][0]; raw[1] &= vmask[kb][1];
-          raw[2] &= vmask[kb][2]; raw[3] &= vmask[kb][3];
+          if (vzero) {
+            // key cbase + 16kb + 8h + e is stored iff 16kb + e lies in [slo, shi)
+            const int slo = ok ? vlo - cbase - 8 * h : 64, shi = vhi - cbase - 8 * h;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int kc = 16 * kb + e;
+              if (kc < slo || kc >= shi) vmask[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+            }
+          }
         }
-        oacc[t] = mfma_32x32x16(__builtin_bit_cast(bf16x8, raw), pb[kb], oacc[t]);
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+          u32x4 raw = *reinterpret_cast<const u32x4*>(buf + T::v_off(32 * t + n, 2 * kb + h));
+          if constexpr (EDGE) {
+            raw[0] &= vmask[0]; raw[1] &= vmask[1]; raw[2] &= vmask[2]; raw[3] &= vmask[3];
+          }
+          oacc[t] = mfma_32x32x16(__builtin_bit_cast(bf16x8, raw), pb, oacc[t]);
+        }
       }
+      l_run += lsum;
+      l_rnd += lsum_r;
     }
   };
 
@@ -313,9 +350,9 @@ void prefill_attn_kernel(ChunkAttnArgs a) {
   // write chunk loc + 1 from the stage into the other tile; load chunk loc + 2 into the stage;
   // compute chunk loc.  Loads past the range read slot 0 and are never computed.
   if (nloc > 0) {
-    int sl_cur = slot_at(0);
-    int sl_nxt = nloc > 1 ? slot_at(1) : -1;
-    int sl_far = nloc > 2 ? slot_at(2) : -1;
+    int sl_cur = slot(fetch(0));
+    int sl_nxt = nloc > 1 ? slot(fetch(1)) : -1;
+    int f_far = fetch(2);                  // slot of chunk loc + 2, still to be converted
     issue(sl_cur);
     commit(&lds[0][0]);
     issue(sl_nxt);
@@ -323,12 +360,12 @@ void prefill_attn_kernel(ChunkAttnArgs a) {
     auto step = [&](int loc, auto edge_tag) __attribute__((always_inline)) {
       lds_barrier();
       commit(&lds[(loc + 1) & 1][0]);
+      const int sl_far = loc + 2 < nloc ? slot(f_far) : -1;
       issue(sl_far);
-      const int sl_more = loc + 3 < nloc ? slot_at(loc + 3) : -1;
+      f_far = fetch(loc + 3);
       compute(&lds[loc & 1][0], loc, sl_cur >= 0, edge_tag);
       sl_cur = sl_nxt;
       sl_nxt = sl_far;
-      sl_far = sl_more;
     };
     // interior chunks [ca, cb): after every row's window start and the stored range's start,
     // ending at or before the tile's first query and the stored range's end
@@ -348,7 +385,8 @@ void prefill_attn_kernel(ChunkAttnArgs a) {
   // ---- epilogue ---------------------------------------------------------------------------------
   if (!row_ok) return;
   const float l = pair_sum(l_run);
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float lr = pair_sum(l_rnd);
+  const float inv = lr > 0.f ? 1.f / lr : 0.f;
   const float lse_nat = l > 0.f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
   float* dst;
   if (a.part_o == nullptr) {

@@ -149,7 +149,11 @@ def test_p3_key_shift_invariance():
 @pytest.mark.parametrize("ctx,q_len,hq,hkv,d,window", [(1024, 16, 8, 2, 64, 0),
                                                        (777, 16, 16, 4, 32, 512),
                                                        (40, 17, 4, 4, 8, 0),
-                                                       (300, 3, 6, 1, 16, 7)])
+                                                       (300, 3, 6, 1, 16, 7),
+                                                       # prefill blocks: a whole prompt at
+                                                       # once, and a long block after others
+                                                       (1024, 1024, 8, 2, 16, 0),
+                                                       (2000, 1024, 4, 1, 16, 512)])
 def test_p4_matches_torch_sdpa(ctx, q_len, hq, hkv, d, window):
     k, v = _rows(10 + ctx, ctx, hkv, d)
     q = np.random.default_rng(11).standard_normal((q_len, hq, d))
@@ -227,6 +231,21 @@ def test_p7_ring_equals_contiguous_window(pos0):
     np.testing.assert_allclose(lse, rl, rtol=0, atol=1e-14)
 
 
+@pytest.mark.parametrize("pos0,q_len", [(30000, 1024), (0, 1024), (1023, 1537)])
+def test_p7_ring_equals_contiguous_window_long_block(pos0, q_len):
+    # a prefill block: window + q_len - 1 positions must fit the ring (1535 / 2048 at 1024)
+    c = ring_case(905, 0, pos0, q_len, 4, 1, 16, 2048, 512)
+    out, lse = oracle.attention_ring(c.q, c.k_ring, c.v_ring, pos0, c.ring_head, 2048, 512)
+    n = c.ctx_len
+    k = np.zeros((n, 1, 16), np.uint16)
+    v = np.zeros((n, 1, 16), np.uint16)
+    k[c.rows_first:] = c.k_rows
+    v[c.rows_first:] = c.v_rows
+    ro, rl = oracle.attention_contiguous(c.q, k, v, n, window=512, dtype="bf16")
+    np.testing.assert_allclose(out, ro, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse, rl, rtol=0, atol=1e-14)
+
+
 def test_p7_ring_slot_rule_and_residency():
     c = ring_case(903, 0, 30000, 16, 4, 1, 8, 2048, 512)
     assert c.ring_head == 1328
@@ -253,6 +272,15 @@ def test_p8_paged_equals_contiguous_any_permutation(ctx):
     for o, l in outs:
         np.testing.assert_array_equal(o, ref[0])
         np.testing.assert_array_equal(l, ref[1])
+
+
+def test_p8_paged_long_block_equals_contiguous():
+    # a 1,000-query block over a permuted pool: every row equals contiguous attention
+    c = paged_case(906, 0, 3000, 1000, 4, 2, 16, n_slots=60, perm="seeded")
+    o, l = oracle.attention_paged(c.q, c.k_pool, c.v_pool, c.page_table, 3000)
+    ro, rl = oracle.attention_contiguous(c.q, c.k_rows, c.v_rows, 3000, dtype="bf16")
+    np.testing.assert_array_equal(o, ro)
+    np.testing.assert_array_equal(l, rl)
 
 
 def test_p8_store_layout_by_element():
