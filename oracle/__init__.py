@@ -23,7 +23,9 @@ What it computes, and where the method is stated:
 * ``cache``: appending the verify block's own K/V rows to the ring and the pool
   before its attention, and committing the accepted ones (slot = pos mod 2048; a
   pool chunk gets a slot when first written and gives it back if the block's rows
-  in it are all rejected), with ``PagerModel``, the slot bookkeeping.
+  in it are all rejected), with ``PagerModel``, the slot bookkeeping; paging whole chunks
+  out to a host chunk store and back in, and attention over the resident subset of the
+  pool (same post, "Three optimizations", item 1).
 
 Parity pins: every function here is pinned in ``tests/test_oracle_*.py`` by
 closed forms, invariants, brute force or a library routine; none is "parity
@@ -34,4 +36,5 @@ from .attention import (attend_rows, attention_contiguous, attention_paged,  # n
                         key_bounds, to_f64)
 from .merge import attention_partial, lse_merge  # noqa: F401
 from .accept import first_argmax, greedy_accept  # noqa: F401
-from .cache import PagerModel, append_paged, append_ring  # noqa: F401
+from .cache import (PAGED_OUT, PagerModel, append_paged, append_ring,  # noqa: F401
+                    attention_resident, page_in, page_out)

@@ -21,6 +21,17 @@ back.  Which free slot is handed out is a policy, not part of the method; ``Page
 states the one the library uses (a stack that starts as 0, 1, 2, ...; a block's unused
 chunks are returned last chunk first, so the earliest is handed out first again).
 
+Host paging (same post, "Three optimizations", item 1: the pool keeps part of the context on the
+GPU, cold 64-token chunks page to host RAM bit-exact, and which chunks stay is a scoring
+question outside this path).  A host chunk store holds one entry per logical chunk, laid out like
+a pool slot; paging a chunk out copies its slot to the chunk's host entry and frees the slot,
+paging it in copies the entry into a free slot.  Attention of a block over the resident subset
+attends exactly the keys of the chunks that have a slot, at their own positions.
+
+Readings: only whole committed chunks (every position below the committed length, and not the
+chunk the next block writes into) can be paged out; a paged-out chunk's table entry is -2; the
+slots freed by a page-out return to the same free stack as the pager's, in the order given.
+
 Stores: K ``[slot][Hkv][64][D]``, V dimension-major ``[slot][Hkv][D][64]`` (as in
 ``attention``).  Arrays are copied, never modified in place.
 """
@@ -28,7 +39,10 @@ from __future__ import annotations
 
 import numpy as np
 
+from .attention import attend_rows, to_f64
+
 CHUNK = 64
+PAGED_OUT = -2
 
 
 def append_ring(k_ring, v_ring, k_new, v_new, pos_first: int):
@@ -56,6 +70,48 @@ def append_paged(k_pool, v_pool, table, k_new, v_new, pos_first: int):
             k[slot, g, p % CHUNK, :] = k_new[i, g, :]
             v[slot, g, :, p % CHUNK] = v_new[i, g, :]
     return k, v
+
+
+def page_out(k_pool, v_pool, slots, chunk_ids, k_host, v_host):
+    """Host entries chunk_ids[i] <- pool slot slots[i] (K and V).  Returns the new host stores."""
+    kh = np.array(k_host, copy=True)
+    vh = np.array(v_host, copy=True)
+    for s, c in zip(slots, chunk_ids):
+        kh[c] = k_pool[s]
+        vh[c] = v_pool[s]
+    return kh, vh
+
+
+def page_in(k_host, v_host, chunk_ids, slots, k_pool, v_pool):
+    """Pool slots slots[i] <- host entries chunk_ids[i] (K and V).  Returns the new pool."""
+    kp = np.array(k_pool, copy=True)
+    vp = np.array(v_pool, copy=True)
+    for c, s in zip(chunk_ids, slots):
+        kp[s] = k_host[c]
+        vp[s] = v_host[c]
+    return kp, vp
+
+
+def attention_resident(q, k_pool, v_pool, chunk_ids, slots, ctx_len, scale=None, dtype="bf16"):
+    """Attention of the block over the resident chunks only: the keys are positions
+    c*64 .. c*64+63 (below ctx_len) of every listed chunk c, read from pool slot slots[i]; query
+    i sits at ctx_len - q_len + i and sees the listed keys at or before its own position."""
+    qf = to_f64(q, dtype)
+    q_len, _, d = qf.shape
+    key_pos, key_slot, key_off = [], [], []
+    for c, s in zip(chunk_ids, slots):
+        for t in range(CHUNK):
+            if c * CHUNK + t < ctx_len:
+                key_pos.append(c * CHUNK + t)
+                key_slot.append(s)
+                key_off.append(t)
+    key_pos = np.array(key_pos, dtype=np.int64)
+    ks, ko = np.array(key_slot, dtype=np.int64), np.array(key_off, dtype=np.int64)
+    kp, vp = np.asarray(k_pool), np.asarray(v_pool)
+    sc = 1.0 / np.sqrt(d) if not scale else float(scale)
+    return attend_rows(qf, lambda g: to_f64(kp[ks, g, ko, :], dtype),
+                       lambda g: to_f64(vp[ks, g, :, ko], dtype), key_pos,
+                       ctx_len - q_len + np.arange(q_len), 0, sc, kp.shape[1])
 
 
 class PagerModel:
@@ -96,3 +152,36 @@ class PagerModel:
             self.free.append(self.table[c])
             self.table[c] = -1
         self.pending = None
+
+    def evict(self, chunk_ids):
+        """Page out whole committed chunks: their slots (returned, in the order given) go back
+        to the free stack and their table entries become PAGED_OUT.  All or nothing."""
+        full = self.ctx // CHUNK                        # chunks whose 64 positions are committed
+        ids = list(chunk_ids)
+        if len(set(ids)) != len(ids) or any(not 0 <= c < full or self.table[c] < 0 for c in ids):
+            raise ValueError("evict")
+        slots = [self.table[c] for c in ids]
+        for c in ids:
+            self.free.append(self.table[c])
+            self.table[c] = PAGED_OUT
+        return slots
+
+    def restore(self, chunk_ids):
+        """Page chunks back in: each gets the next free slot (returned, in the order given)."""
+        ids = list(chunk_ids)
+        if len(set(ids)) != len(ids) or any(not 0 <= c < len(self.table) or
+                                            self.table[c] != PAGED_OUT for c in ids):
+            raise ValueError("restore")
+        if len(ids) > len(self.free):
+            raise MemoryError("pool exhausted")
+        slots = []
+        for c in ids:
+            s = self.free.pop()
+            self.table[c] = s
+            slots.append(s)
+        return slots
+
+    def resident(self):
+        """(chunk ids, slots) of every chunk that has a slot, in increasing chunk order."""
+        ids = [c for c, s in enumerate(self.table) if s >= 0]
+        return ids, [self.table[c] for c in ids]

@@ -166,3 +166,153 @@ def test_pager_model_policy_and_errors():
     with pytest.raises(MemoryError):
         p.reserve(1000)                                  # table has 8 chunks, 1 used
     assert p.pending is None and p.ctx == 64
+
+
+# --- host paging and the resident subset -----------------------------------------------------
+
+def _pool_case(seed, ctx, hkv=2, d=16, n_slots=None, q_len=16, hq=4):
+    from synth import paged_case
+    return paged_case(seed, 0, ctx, q_len, hq, hkv, d, n_slots=n_slots)
+
+
+def test_page_out_in_round_trip_is_bit_exact():
+    c = _pool_case(41, 1000, n_slots=24)
+    nch = -(-1000 // CH)
+    kh = np.zeros((nch,) + c.k_pool.shape[1:], np.uint16)
+    vh = np.zeros((nch,) + c.v_pool.shape[1:], np.uint16)
+    ids = [3, 5, 6, 0]
+    slots = [int(c.page_table[i]) for i in ids]
+    kh, vh = oracle.page_out(c.k_pool, c.v_pool, slots, ids, kh, vh)
+    for i, s in zip(ids, slots):
+        np.testing.assert_array_equal(kh[i], c.k_pool[s])
+        np.testing.assert_array_equal(vh[i], c.v_pool[s])
+    assert not np.any(kh[[1, 2, 4]])                      # other entries untouched
+    # back into other slots: the same bits at the new places, and the same attention
+    free = [s for s in range(24) if s not in set(c.page_table.tolist())]
+    new = free[:4]
+    kp, vp = oracle.page_in(kh, vh, ids, new, c.k_pool, c.v_pool)
+    for s_old, s_new in zip(slots, new):
+        np.testing.assert_array_equal(kp[s_new], c.k_pool[s_old])
+        np.testing.assert_array_equal(vp[s_new], c.v_pool[s_old])
+    pt = c.page_table.copy()
+    pt[ids] = new
+    a = oracle.attention_paged(c.q, c.k_pool, c.v_pool, c.page_table, 1000)
+    b = oracle.attention_paged(c.q, kp, vp, pt, 1000)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_resident_all_chunks_equals_paged():
+    c = _pool_case(42, 1500)
+    ids = list(range(-(-1500 // CH)))
+    got = oracle.attention_resident(c.q, c.k_pool, c.v_pool, ids, c.page_table[ids].tolist(), 1500)
+    want = oracle.attention_paged(c.q, c.k_pool, c.v_pool, c.page_table, 1500)
+    np.testing.assert_array_equal(got[0], want[0])
+    np.testing.assert_array_equal(got[1], want[1])
+
+
+@pytest.mark.parametrize("ctx,q_len,keep", [(1500, 16, (0, 3, 7, 8, 20, 21, 22, 23)),
+                                           (3000, 200, (1, 2, 10, 40, 43, 44, 45, 46)),
+                                           (640, 70, (8, 9))])
+def test_resident_subset_matches_sdpa_with_mask(ctx, q_len, keep):
+    import torch
+    c = _pool_case(43, ctx, q_len=q_len)
+    ids = list(keep)
+    got = oracle.attention_resident(c.q, c.k_pool, c.v_pool, ids, c.page_table[ids].tolist(), ctx)
+    # library routine over the contiguous rows, keys limited to the resident chunks
+    G = 2
+    q = torch.from_numpy(oracle.bf16_to_f64(c.q)).permute(1, 0, 2)[None]
+    k = torch.from_numpy(oracle.bf16_to_f64(c.k_rows)).permute(1, 0, 2).repeat_interleave(G, 0)[None]
+    v = torch.from_numpy(oracle.bf16_to_f64(c.v_rows)).permute(1, 0, 2).repeat_interleave(G, 0)[None]
+    qp = torch.arange(ctx - q_len, ctx)[:, None]
+    kp = torch.arange(ctx)[None, :]
+    mask = (kp <= qp) & torch.isin(kp // CH, torch.tensor(ids))
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask)
+    np.testing.assert_allclose(got[0], ref[0].permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("ctx,q_len,keep", [(1500, 16, (0, 3, 7, 23)),
+                                           (3000, 200, (2, 10, 43, 44, 45, 46)),
+                                           (4096, 64, (5, 63))])
+def test_resident_equals_packed_pool_at_a_shorter_context(ctx, q_len, keep):
+    # the reading the library's resident call uses: with the block's chunks at the end of the
+    # list, every earlier resident chunk is wholly visible, so the attention equals attention
+    # over the packed slot list at ctx - 64 * (chunks missing before the block's first chunk)
+    c = _pool_case(44, ctx, q_len=q_len)
+    ids = list(keep)
+    slots = c.page_table[ids].tolist()
+    got = oracle.attention_resident(c.q, c.k_pool, c.v_pool, ids, slots, ctx)
+    first = (ctx - q_len) // CH
+    missing = first - ids.index(first)
+    virt = oracle.attention_paged(c.q, c.k_pool, c.v_pool, np.array(slots), ctx - CH * missing)
+    np.testing.assert_allclose(got[0], virt[0], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(got[1], virt[1], rtol=0, atol=1e-13)
+
+
+def test_pager_model_evict_restore_policy_and_errors():
+    p = oracle.PagerModel(6, 10)
+    p.reserve(200)                                       # chunks 0..3 -> slots 0..3
+    p.commit(200)                                        # ctx 200: chunks 0, 1, 2 full, 3 partial
+    assert p.evict([1, 0]) == [1, 0]
+    assert p.table[:4] == [oracle.PAGED_OUT, oracle.PAGED_OUT, 2, 3] and p.free[-2:] == [1, 0]
+    assert p.resident() == ([2, 3], [2, 3])
+    for bad in ([3], [0], [2, 2], [-1], [7]):            # partial tail, already out, twice, range
+        with pytest.raises(ValueError):
+            p.evict(bad)
+    assert p.restore([1]) == [0]                         # the last freed slot first
+    with pytest.raises(ValueError):
+        p.restore([2])                                   # resident
+    p.reserve(100)                                       # a block while chunk 0 is out
+    assert p.resident()[0] == [1, 2, 3, 4]
+    with pytest.raises(ValueError):
+        p.evict([3])                                     # the chunk the pending block writes
+    p.commit(100)                                        # ctx 300: chunks 0..3 full
+    assert p.evict([3, 2]) == [3, 2]
+    assert p.restore([0, 2, 3]) == [2, 3, 4]
+    # not enough free slots: nothing changes
+    q = oracle.PagerModel(2, 4)
+    q.reserve(128)
+    q.commit(128)
+    q.evict([0, 1])
+    q.reserve(64)
+    q.commit(64)
+    before = (list(q.table), list(q.free))
+    with pytest.raises(MemoryError):
+        q.restore([0, 1])
+    assert (q.table, q.free) == before
+
+
+def test_pager_model_paging_invariants_random():
+    g = np.random.default_rng(45)
+    p = oracle.PagerModel(20, 80)
+    for _ in range(300):
+        op = g.integers(0, 3)
+        if op == 0:
+            n = int(g.integers(1, 200))
+            try:
+                p.reserve(n)
+            except MemoryError:
+                continue
+            p.commit(int(g.integers(0, n + 1)))
+        elif op == 1:
+            full = p.ctx // CH
+            cand = [c for c in range(full) if p.table[c] >= 0]
+            if cand:
+                pick = list(g.choice(cand, size=min(len(cand), int(g.integers(1, 4))), replace=False))
+                p.evict([int(c) for c in pick])
+        else:
+            out = [c for c, s in enumerate(p.table) if s == oracle.PAGED_OUT]
+            if out:
+                pick = [int(c) for c in g.choice(out, size=min(len(out), 2), replace=False)]
+                try:
+                    p.restore(pick)
+                except MemoryError:
+                    pass
+        used = [s for s in p.table if s >= 0]
+        assert len(used) == len(set(used))
+        assert sorted(used + p.free) == list(range(20))
+        nc = -(-p.ctx // CH)
+        assert all(s != -1 for s in p.table[:nc])             # committed: resident or paged out
+        assert all(s == -1 for s in p.table[nc:])
+        ids, slots = p.resident()
+        assert ids == sorted(ids) and all(p.table[c] == s for c, s in zip(ids, slots))

@@ -158,3 +158,75 @@ def test_cache_pins_catch_planted_mistakes(kind, monkeypatch):
     monkeypatch.setattr(oracle, "append_paged", ap)
     monkeypatch.setattr(oracle, "PagerModel", P)
     assert not sequence_matches(seed=1, q_len=16, ring=256, window=100, prefill=150)
+
+
+# --- host paging and the resident subset: planted mistakes --------------------------------------
+
+def _resident_mutant(kind):
+    from oracle import cache as C
+
+    def attention_resident(q, k_pool, v_pool, chunk_ids, slots, ctx_len, scale=None, dtype="bf16"):
+        qf = A.to_f64(q, dtype)
+        q_len, _, d = qf.shape
+        pos, ks, ko = [], [], []
+        for c, s in zip(chunk_ids, slots):
+            base = s if kind == "slot_as_position" else c
+            for t in range(C.CHUNK):
+                if kind == "no_context_bound" or c * C.CHUNK + t < ctx_len:
+                    pos.append(base * C.CHUNK + t)
+                    ks.append(s)
+                    ko.append(t)
+        pos, ks, ko = np.array(pos), np.array(ks), np.array(ko)
+        kp, vp = np.asarray(k_pool), np.asarray(v_pool)
+        return A.attend_rows(qf, lambda g: A.to_f64(kp[ks, g, ko, :], dtype),
+                             lambda g: A.to_f64(vp[ks, g, :, ko], dtype), pos,
+                             ctx_len - q_len + np.arange(q_len), 0, 1.0 / math.sqrt(d),
+                             kp.shape[1])
+    return attention_resident
+
+
+@pytest.mark.parametrize("kind", ["slot_as_position", "no_context_bound"])
+def test_resident_pins_catch_planted_mistakes(kind, monkeypatch):
+    from test_oracle_cache import test_resident_subset_matches_sdpa_with_mask as pin
+    pin(1500, 16, (0, 3, 7, 8, 20, 21, 22, 23))
+    monkeypatch.setattr(oracle, "attention_resident", _resident_mutant(kind))
+    with pytest.raises(AssertionError):
+        pin(1500, 16, (0, 3, 7, 8, 20, 21, 22, 23))
+
+
+def test_page_out_without_v_is_caught(monkeypatch):
+    from test_oracle_cache import test_page_out_in_round_trip_is_bit_exact as pin
+
+    def page_out(k_pool, v_pool, slots, chunk_ids, k_host, v_host):
+        kh, vh = np.array(k_host, copy=True), np.array(v_host, copy=True)
+        for s, c in zip(slots, chunk_ids):
+            kh[c] = k_pool[s]
+        return kh, vh
+
+    pin()
+    monkeypatch.setattr(oracle, "page_out", page_out)
+    with pytest.raises(AssertionError):
+        pin()
+
+
+def test_evicting_the_partial_tail_chunk_is_caught(monkeypatch):
+    from test_oracle_cache import test_pager_model_evict_restore_policy_and_errors as pin
+    from oracle import cache as C
+
+    class Pager(C.PagerModel):
+        def evict(self, chunk_ids):
+            full = -(-self.ctx // C.CHUNK)             # ceil: the partly written chunk too
+            ids = list(chunk_ids)
+            if len(set(ids)) != len(ids) or any(not 0 <= c < full or self.table[c] < 0
+                                                for c in ids):
+                raise ValueError("evict")
+            slots = [self.table[c] for c in ids]
+            for c in ids:
+                self.free.append(self.table[c])
+                self.table[c] = C.PAGED_OUT
+            return slots
+
+    pin()
+    monkeypatch.setattr(oracle, "PagerModel", Pager)
+    with pytest.raises((AssertionError, pytest.fail.Exception)):   # "DID NOT RAISE"
+        pin()
