@@ -269,7 +269,8 @@ rkv_pager* rkv_pager_create(int32_t n_slots, int32_t n_table);   /* NULL on size
 void rkv_pager_destroy(rkv_pager* p);
 int64_t rkv_pager_ctx_len(const rkv_pager* p);                    /* -1 for NULL */
 int32_t rkv_pager_free_slots(const rkv_pager* p);                 /* -1 for NULL */
-/* host copy of table entries 0 .. n-1 into out (-1: no slot); n <= n_table */
+/* host copy of table entries 0 .. n-1 into out (-1: no slot, RKV_PAGED_OUT: on the host);
+ * n <= n_table */
 int32_t rkv_pager_table(const rkv_pager* p, int32_t* out, int32_t n);
 int32_t rkv_pager_reserve(rkv_pager* p, int32_t n, int32_t* first_chunk, int32_t* n_new,
                           int32_t* slots);
@@ -289,6 +290,73 @@ int32_t verify_kv_append_paged(const void* k_new, const void* v_new, int32_t n,
                                void* k_pool, void* v_pool, int32_t* page_table,
                                int32_t n_table, int32_t n_slots, int32_t first_chunk,
                                int32_t n_new, const int32_t* new_slots, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Host paging of the pool (lucebox post, "Three optimizations", item 1: the pool keeps part of
+ * the context on the GPU and cold 64-token chunks page to host RAM bit-exact; which chunks
+ * stay resident is scored by the drafter, outside this library).
+ *
+ * Host chunk store: k_host [n_host][Hkv][64][D], v_host [n_host][Hkv][D][64] bf16 in host
+ * memory, one entry per logical chunk (entry c holds chunk c), laid out like a pool slot.
+ * Allocate it pinned (hipHostMalloc) so that the copies run asynchronously; pageable memory
+ * works, but the copies then wait for the host.
+ *   kv_page_out  pool slot slots[i] -> host entry chunk_ids[i], i < n (K and V, bit-exact)
+ *   kv_page_in   host entry chunk_ids[i] -> pool slot slots[i]
+ * slots and chunk_ids are host arrays, read before the call returns; chunk ids must be
+ * distinct in a page-out and slots distinct in a page-in.  Both calls go through a device
+ * workspace of kv_page_workspace_bytes(n_kv_heads, head_dim, n) bytes: a kernel packs the
+ * chunks there (or unpacks them), and they cross PCIe with one copy per run of consecutive
+ * chunk ids, RKV_PAGE_BATCH chunks at a time.  Both are asynchronous on `stream`: the host
+ * entries (page-out) or the slots (page-in) hold the data once the stream has passed the
+ * call, and a slot freed by a page-out may be rewritten by any later work on that stream.
+ * Status: RKV_ERR_NULL; RKV_ERR_SHAPE (head counts, head_dim); RKV_ERR_ARG (n < 0, a chunk id
+ * outside [0, n_host), a repeated chunk id or slot); RKV_ERR_TABLE (a slot outside
+ * [0, n_slots)); RKV_ERR_WORKSPACE; RKV_ERR_HIP.
+ * ------------------------------------------------------------------------------- */
+#define RKV_PAGE_BATCH 256
+size_t kv_page_workspace_bytes(int32_t n_kv_heads, int32_t head_dim, int32_t n);
+int32_t kv_page_out(const void* k_pool, const void* v_pool, int32_t n_kv_heads,
+                    int32_t head_dim, int32_t n_slots, const int32_t* slots,
+                    const int32_t* chunk_ids, int32_t n, void* k_host, void* v_host,
+                    int64_t n_host, void* workspace, size_t workspace_bytes, void* stream);
+int32_t kv_page_in(const void* k_host, const void* v_host, int64_t n_host,
+                   const int32_t* chunk_ids, const int32_t* slots, int32_t n, void* k_pool,
+                   void* v_pool, int32_t n_kv_heads, int32_t head_dim, int32_t n_slots,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Full-attention attention of a block (verify or prefill) over the resident subset of the
+ * pool: the keys are the positions of the chunks listed in chunk_ids (host array, strictly
+ * increasing, n_res >= 1 entries); chunk chunk_ids[i] is read from pool slot d_slots[i]
+ * (device array).  Query i sits at ctx_len - q_len + i and sees the listed keys at or before
+ * its position.  The chunks holding the block's positions (ctx_len-q_len .. ctx_len-1) must be
+ * listed, as the last entries (RKV_ERR_TABLE otherwise); positions >= ctx_len in the last
+ * chunk may hold anything.  Every earlier listed chunk is then wholly visible to every query,
+ * so the call runs the paged kernels with d_slots as the table at the context
+ * ctx_len - 64 * (chunks missing before the block's first chunk), n_res chunks long.  Splits
+ * and outputs: as verify_attn_paged over n_res chunks; the workspace is
+ * verify_attn_paged_workspace_bytes(dims, 64 * n_res, 64, num_splits) bytes. */
+int32_t verify_attn_paged_resident(const rkv_attn_dims* dims, const void* q,
+                                   const void* k_pool, const void* v_pool,
+                                   const int32_t* d_slots, const int32_t* chunk_ids,
+                                   int32_t n_res, int32_t n_slots, int64_t ctx_len,
+                                   int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                   float* out, float* lse, void* stream);
+
+/* The pager's side of host paging.  A chunk paged out has the table entry RKV_PAGED_OUT.
+ *   rkv_pager_evict    n whole committed chunks (chunk < floor(ctx/64)) that have a slot: their
+ *                      slots are written to slots[] (copy them out with kv_page_out before any
+ *                      reuse) and return to the free list in the order given.
+ *   rkv_pager_restore  n paged-out chunks each get the next free slot (slots[] out; copy the
+ *                      data in with kv_page_in).
+ *   rkv_pager_resident the chunks that have a slot (the pending block's included), in
+ *                      increasing order: returns how many; writes up to cap of them to
+ *                      chunk_ids and slots (both may be NULL when cap is 0).
+ * All or nothing: RKV_ERR_ARG for a chunk that does not qualify or is repeated, RKV_ERR_TABLE
+ * when the free list is too short for a restore, RKV_ERR_NULL for null pointers. */
+#define RKV_PAGED_OUT (-2)
+int32_t rkv_pager_evict(rkv_pager* p, const int32_t* chunk_ids, int32_t n, int32_t* slots);
+int32_t rkv_pager_restore(rkv_pager* p, const int32_t* chunk_ids, int32_t n, int32_t* slots);
+int32_t rkv_pager_resident(const rkv_pager* p, int32_t* chunk_ids, int32_t* slots, int32_t cap);
 
 #ifdef __cplusplus
 }

@@ -63,6 +63,16 @@ _PROTOS = {
                                         c_int32, _P]),
     "verify_kv_append_paged": (c_int32, [_P, _P, c_int32, c_int64, c_int32, c_int32, _P, _P, _P,
                                          c_int32, c_int32, c_int32, c_int32, _P, _P]),
+    "kv_page_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
+    "kv_page_out": (c_int32, [_P, _P, c_int32, c_int32, c_int32, _P, _P, c_int32, _P, _P, c_int64,
+                              _P, c_size_t, _P]),
+    "kv_page_in": (c_int32, [_P, _P, c_int64, _P, _P, c_int32, _P, _P, c_int32, c_int32, c_int32,
+                             _P, c_size_t, _P]),
+    "verify_attn_paged_resident": (c_int32, [_DIMS, _P, _P, _P, _P, _P, c_int32, c_int32, c_int64,
+                                             c_int32, _P, c_size_t, _P, _P, _P]),
+    "rkv_pager_evict": (c_int32, [c_void_p, _P, c_int32, _P]),
+    "rkv_pager_restore": (c_int32, [c_void_p, _P, c_int32, _P]),
+    "rkv_pager_resident": (c_int32, [c_void_p, _P, _P, c_int32]),
 }
 
 _lib = None

@@ -285,6 +285,33 @@ class Pager:
     def commit(self, n_keep: int):
         check("rkv_pager_commit", self._L.rkv_pager_commit(self._p, n_keep))
 
+    def evict(self, chunk_ids):
+        """Page whole committed chunks out: their slots (to copy out with kv_page_out before
+        any reuse), in the order given."""
+        n = len(chunk_ids)
+        ids = (ctypes.c_int32 * max(1, n))(*chunk_ids)
+        slots = (ctypes.c_int32 * max(1, n))()
+        check("rkv_pager_evict", self._L.rkv_pager_evict(self._p, ids, n, slots))
+        return list(slots)[:n]
+
+    def restore(self, chunk_ids):
+        """Give paged-out chunks slots again (to copy in with kv_page_in), in the order given."""
+        n = len(chunk_ids)
+        ids = (ctypes.c_int32 * max(1, n))(*chunk_ids)
+        slots = (ctypes.c_int32 * max(1, n))()
+        check("rkv_pager_restore", self._L.rkv_pager_restore(self._p, ids, n, slots))
+        return list(slots)[:n]
+
+    def resident(self):
+        """(chunk ids, slots) of the chunks that have a slot, in increasing chunk order."""
+        k = self._L.rkv_pager_resident(self._p, None, None, 0)
+        if k < 0:
+            check("rkv_pager_resident", k)
+        ids = (ctypes.c_int32 * max(1, k))()
+        slots = (ctypes.c_int32 * max(1, k))()
+        self._L.rkv_pager_resident(self._p, ids, slots, k)
+        return list(ids)[:k], list(slots)[:k]
+
 
 def verify_kv_append_ring(k_new, v_new, pos_first: int, k_ring, v_ring, *, stream=None):
     """Append a verify block's rows k_new, v_new [n][Hkv][D] (positions pos_first..) to the
@@ -314,6 +341,88 @@ def verify_kv_append_paged(k_new, v_new, ctx_len: int, k_pool, v_pool, page_tabl
         _ptr(k_new), _ptr(v_new), n, ctx_len, hkv, d, _ptr(k_pool), _ptr(v_pool),
         _ptr(page_table), page_table.numel(), k_pool.shape[0], first_chunk, len(new_slots),
         slots, _stream(stream, dev)))
+
+
+def _host_store(t: torch.Tensor, name: str, ndim: int = 4):
+    if not isinstance(t, torch.Tensor) or t.is_cuda:
+        raise ValueError(f"{name} must be a host tensor (pinned for asynchronous copies)")
+    if not t.is_contiguous() or t.dtype != torch.bfloat16 or t.dim() != ndim:
+        raise ValueError(f"{name} must be a contiguous bf16 [chunks][Hkv][..][..] host tensor")
+
+
+def kv_page_out(k_pool, v_pool, slots, chunk_ids, k_host, v_host, *, workspace=None,
+                stream=None):
+    """Copy pool slots[i] to host entries chunk_ids[i] (K and V, bit-exact), asynchronously on
+    the stream; k_host [n_host][Hkv][64][D], v_host [n_host][Hkv][D][64] host tensors."""
+    _need(k_pool, "k_pool", torch.bfloat16, 4)
+    dev = k_pool.device
+    _need(v_pool, "v_pool", torch.bfloat16, 4, dev)
+    _host_store(k_host, "k_host")
+    _host_store(v_host, "v_host")
+    n_slots, hkv, _, d = k_pool.shape
+    n = len(slots)
+    if len(chunk_ids) != n:
+        raise ValueError("slots and chunk_ids differ in length")
+    L = lib()
+    ws, wsb = _workspace(L.kv_page_workspace_bytes(hkv, d, n), dev, workspace)
+    sl = (ctypes.c_int32 * max(1, n))(*slots)
+    ci = (ctypes.c_int32 * max(1, n))(*chunk_ids)
+    check("kv_page_out", L.kv_page_out(
+        _ptr(k_pool), _ptr(v_pool), hkv, d, n_slots, sl, ci, n,
+        ctypes.c_void_p(k_host.data_ptr()), ctypes.c_void_p(v_host.data_ptr()),
+        k_host.shape[0], _ptr(ws), wsb, _stream(stream, dev)))
+    return ws
+
+
+def kv_page_in(k_host, v_host, chunk_ids, slots, k_pool, v_pool, *, workspace=None,
+               stream=None):
+    """Copy host entries chunk_ids[i] into pool slots[i] (K and V, bit-exact), asynchronously
+    on the stream."""
+    _need(k_pool, "k_pool", torch.bfloat16, 4)
+    dev = k_pool.device
+    _need(v_pool, "v_pool", torch.bfloat16, 4, dev)
+    _host_store(k_host, "k_host")
+    _host_store(v_host, "v_host")
+    n_slots, hkv, _, d = k_pool.shape
+    n = len(slots)
+    if len(chunk_ids) != n:
+        raise ValueError("slots and chunk_ids differ in length")
+    L = lib()
+    ws, wsb = _workspace(L.kv_page_workspace_bytes(hkv, d, n), dev, workspace)
+    sl = (ctypes.c_int32 * max(1, n))(*slots)
+    ci = (ctypes.c_int32 * max(1, n))(*chunk_ids)
+    check("kv_page_in", L.kv_page_in(
+        ctypes.c_void_p(k_host.data_ptr()), ctypes.c_void_p(v_host.data_ptr()), k_host.shape[0],
+        ci, sl, n, _ptr(k_pool), _ptr(v_pool), hkv, d, n_slots, _ptr(ws), wsb,
+        _stream(stream, dev)))
+    return ws
+
+
+def verify_attn_paged_resident(q, k_pool, v_pool, d_slots, chunk_ids, ctx_len: int, *,
+                               num_splits: int = 0, scale: float = 0.0, out=None, lse=None,
+                               want_lse: bool = True, workspace=None, stream=None):
+    """Full-attention attention of the block over the resident chunks only: chunk_ids (host
+    list, increasing) read from the device slot list d_slots."""
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _need(k_pool, "k_pool", torch.bfloat16, 4, dev)
+    _need(v_pool, "v_pool", torch.bfloat16, 4, dev)
+    _need(d_slots, "d_slots", torch.int32, 1, dev)
+    n_slots, hkv, chunk, d = k_pool.shape
+    n_res = len(chunk_ids)
+    if d_slots.numel() != n_res:
+        raise ValueError("d_slots and chunk_ids differ in length")
+    dims = _dims(q, hkv, scale)
+    L = lib()
+    # the call runs over n_res chunks: its splits and workspace are those of 64 * n_res positions
+    ws, wsb = _workspace(L.verify_attn_paged_workspace_bytes(ctypes.byref(dims), chunk * n_res,
+                                                             chunk, num_splits), dev, workspace)
+    out, lse = _outputs(q, out, lse, want_lse)
+    ci = (ctypes.c_int32 * max(1, n_res))(*chunk_ids)
+    check("verify_attn_paged_resident", L.verify_attn_paged_resident(
+        ctypes.byref(dims), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(d_slots), ci, n_res,
+        n_slots, ctx_len, num_splits, _ptr(ws), wsb, _ptr(out), _ptr(lse), _stream(stream, dev)))
+    return out, lse
 
 
 def tensor_from_numpy(arr, device="cuda", bf16_bits: Optional[bool] = None) -> torch.Tensor:

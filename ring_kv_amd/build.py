@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libring_kv.so")
 PROBE_LIB = os.path.join(HERE, "libring_kv_probe.so")
 PROBE_SRC = "probe.hip"
 SOURCES = ["abi.hip", "attn_chunked.hip", "attn_prefill.hip", "attn_merge.hip",
-           "attn_contig.hip", "accept.hip", "layout.hip", "pager.cpp"]
+           "attn_contig.hip", "accept.hip", "layout.hip", "paging.hip", "pager.cpp"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms stay off: hipcc would otherwise form v_pk_* f32 ops from plain float

@@ -347,6 +347,34 @@ int32_t verify_attn_paged(const rkv_attn_dims* dims, const void* q, const void* 
   return run_chunk_attn(a, dims, workspace, out, lse, static_cast<hipStream_t>(stream));
 }
 
+int32_t verify_attn_paged_resident(const rkv_attn_dims* dims, const void* q,
+                                   const void* k_pool, const void* v_pool,
+                                   const int32_t* d_slots, const int32_t* chunk_ids,
+                                   int32_t n_res, int32_t n_slots, int64_t ctx_len,
+                                   int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                   float* out, float* lse, void* stream) {
+  int32_t st = check_dims(dims);
+  if (st != RKV_OK) return st;
+  if (chunk_ids == nullptr) return RKV_ERR_NULL;
+  if (ctx_len < dims->q_len) return RKV_ERR_SHAPE;
+  if (n_res < 1) return RKV_ERR_TABLE;
+  for (int32_t i = 0; i < n_res; ++i)
+    if (chunk_ids[i] < 0 || (i > 0 && chunk_ids[i] <= chunk_ids[i - 1])) return RKV_ERR_TABLE;
+  // the block's chunks must close the list, in order
+  const int64_t first = (ctx_len - dims->q_len) / kChunk;
+  const int64_t last = (ctx_len - 1) / kChunk;
+  const int64_t nb = last - first + 1;
+  if (nb > n_res) return RKV_ERR_TABLE;
+  for (int64_t j = 0; j < nb; ++j)
+    if (chunk_ids[n_res - nb + j] != first + j) return RKV_ERR_TABLE;
+  // every listed chunk before the block's first is wholly visible: the packed list is a page
+  // table at a context shorter by the chunks that are not listed
+  const int64_t missing = first - (n_res - nb);
+  return verify_attn_paged(dims, q, k_pool, v_pool, d_slots, n_res, n_slots, kChunk,
+                           ctx_len - kChunk * missing, num_splits, workspace, workspace_bytes,
+                           out, lse, stream);
+}
+
 int32_t verify_attn_paged_partial(const rkv_attn_dims* dims, const void* q,
                                   const void* k_pool, const void* v_pool,
                                   const int32_t* page_table, int32_t n_table, int32_t n_slots,

@@ -3,16 +3,19 @@
 // 152 tok/s at 256K context", "Three optimizations", item 1: the full-attention layers keep
 // 64-token chunks in a pool located through a page table).  A verify block first reserves the
 // chunks its rows start, and after the accept commits the rows it keeps; chunks that end up
-// holding no committed position return to the free list.
+// holding no committed position return to the free list.  Whole committed chunks can be paged
+// out to host memory (their slots return to the free list) and back in (same post, same item:
+// cold chunks page to host RAM).
 #include "ring_kv.h"
 
+#include <algorithm>
 #include <cstdint>
 #include <new>
 #include <vector>
 
 struct rkv_pager {
   int32_t n_slots;
-  std::vector<int32_t> table;     // logical chunk -> slot, -1 for none
+  std::vector<int32_t> table;     // logical chunk -> slot, -1 for none, RKV_PAGED_OUT on the host
   std::vector<int32_t> free;      // stack: back() is handed out next
   int64_t ctx = 0;                // committed positions
   // the pending block (between reserve and commit)
@@ -99,6 +102,63 @@ int32_t rkv_pager_commit(rkv_pager* p, int32_t n_keep) {
   p->pending = false;
   p->pend_n = p->pend_first = p->pend_new = 0;
   return RKV_OK;
+}
+
+int32_t rkv_pager_evict(rkv_pager* p, const int32_t* chunk_ids, int32_t n, int32_t* slots) {
+  if (p == nullptr || ((chunk_ids == nullptr || slots == nullptr) && n > 0)) return RKV_ERR_NULL;
+  if (n < 0) return RKV_ERR_ARG;
+  const int64_t full = p->ctx / kChunk;             // chunks whose 64 positions are committed
+  std::vector<int32_t> seen(chunk_ids, chunk_ids + n);
+  std::sort(seen.begin(), seen.end());
+  if (std::adjacent_find(seen.begin(), seen.end()) != seen.end()) return RKV_ERR_ARG;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t c = chunk_ids[i];
+    if (c < 0 || c >= full || p->table[(size_t)c] < 0) return RKV_ERR_ARG;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const size_t c = (size_t)chunk_ids[i];
+    slots[i] = p->table[c];
+    p->free.push_back(p->table[c]);
+    p->table[c] = RKV_PAGED_OUT;
+  }
+  return RKV_OK;
+}
+
+int32_t rkv_pager_restore(rkv_pager* p, const int32_t* chunk_ids, int32_t n, int32_t* slots) {
+  if (p == nullptr || ((chunk_ids == nullptr || slots == nullptr) && n > 0)) return RKV_ERR_NULL;
+  if (n < 0) return RKV_ERR_ARG;
+  std::vector<int32_t> seen(chunk_ids, chunk_ids + n);
+  std::sort(seen.begin(), seen.end());
+  if (std::adjacent_find(seen.begin(), seen.end()) != seen.end()) return RKV_ERR_ARG;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t c = chunk_ids[i];
+    if (c < 0 || c >= (int32_t)p->table.size() || p->table[(size_t)c] != RKV_PAGED_OUT)
+      return RKV_ERR_ARG;
+  }
+  if (n > (int32_t)p->free.size()) return RKV_ERR_TABLE;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t s = p->free.back();
+    p->free.pop_back();
+    p->table[(size_t)chunk_ids[i]] = s;
+    slots[i] = s;
+  }
+  return RKV_OK;
+}
+
+int32_t rkv_pager_resident(const rkv_pager* p, int32_t* chunk_ids, int32_t* slots, int32_t cap) {
+  if (p == nullptr) return RKV_ERR_NULL;
+  if (cap < 0) return RKV_ERR_ARG;
+  if (cap > 0 && (chunk_ids == nullptr || slots == nullptr)) return RKV_ERR_NULL;
+  int32_t k = 0;
+  for (size_t c = 0; c < p->table.size(); ++c) {
+    if (p->table[c] < 0) continue;
+    if (k < cap) {
+      chunk_ids[k] = (int32_t)c;
+      slots[k] = p->table[c];
+    }
+    ++k;
+  }
+  return k;
 }
 
 }  // extern "C"

@@ -106,4 +106,16 @@ struct ScatterArgs {
 };
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t stream);
 
+// Whole chunks between pool slots and the packed staging area of a host page-out / page-in.
+struct PageArgs {
+  uint8_t* pool_k;        // [n_slots][chunk_bytes]
+  uint8_t* pool_v;
+  uint8_t* stage;         // [2][n][chunk_bytes]: the K blocks, then the V blocks
+  int64_t chunk_bytes;    // n_kv_heads * 64 * head_dim * 2, a multiple of 16
+  int32_t n;              // chunks in this batch, 1 .. RKV_PAGE_BATCH
+  int32_t to_stage;       // 1: pool -> staging, 0: staging -> pool
+  int32_t slots[RKV_PAGE_BATCH];
+};
+hipError_t launch_page_copy(const PageArgs& a, hipStream_t stream);
+
 }  // namespace rkv

@@ -164,3 +164,65 @@ def test_append_checks():
     assert app_p(ctx=640, first=10, n_new=1) == ETABLE      # past the table
     assert app_p(n_slots=5) == ETABLE                       # slot 5 out of range
     assert app_p(n=0) == EARG and app_p(ctx=-1) == EARG
+
+
+def _i32(*v):
+    return (ctypes.c_int32 * max(1, len(v)))(*v)
+
+
+def test_page_copy_checks():
+    # every case is refused on the host before any HIP call
+    ws = L.kv_page_workspace_bytes(4, 128, 3)
+    assert ws == 2 * 3 * 4 * 64 * 128 * 2
+    assert L.kv_page_workspace_bytes(4, 128, 1000) == 2 * 256 * 4 * 64 * 128 * 2
+    assert L.kv_page_workspace_bytes(4, 96, 3) == 0 and L.kv_page_workspace_bytes(4, 128, 0) == 0
+    out = lambda sl, ci, n, n_slots=16, n_host=100, wsp=P, wsb=ws, d=128: L.kv_page_out(  # noqa: E731
+        P, P, 4, d, n_slots, sl, ci, n, P, P, n_host, wsp, wsb, NULL)
+    inn = lambda sl, ci, n, n_slots=16, n_host=100, wsp=P, wsb=ws: L.kv_page_in(  # noqa: E731
+        P, P, n_host, ci, sl, n, P, P, 4, 128, n_slots, wsp, wsb, NULL)
+    for f in (out, inn):
+        assert f(_i32(0, 1, 2), _i32(5, 6, 7), 0) == OK                   # nothing to copy
+        assert f(_i32(0, 1, 2), _i32(5, 6, 7), -1) == EARG
+        assert f(_i32(0, 1, 16), _i32(5, 6, 7), 3) == ETABLE               # slot past the pool
+        assert f(_i32(0, 1, -1), _i32(5, 6, 7), 3) == ETABLE
+        assert f(_i32(0, 1, 2), _i32(5, 6, 100), 3) == EARG                # chunk past the store
+        assert f(_i32(0, 1, 2), _i32(5, 6, 7), 3, wsp=NULL) == EWS
+        assert f(_i32(0, 1, 2), _i32(5, 6, 7), 3, wsb=ws - 1) == EWS
+        assert f(NULL, _i32(5, 6, 7), 3) == ENULL
+    assert out(_i32(0, 1, 2), _i32(5, 6, 7), 3, d=96) == ESHAPE
+    assert out(_i32(0, 1, 2), _i32(5, 5, 7), 3) == EARG                    # one host entry twice
+    assert inn(_i32(0, 0, 2), _i32(5, 6, 7), 3) == EARG                    # one slot twice
+    assert L.kv_page_out(NULL, P, 4, 128, 16, _i32(0), _i32(0), 1, P, P, 100, P, ws, NULL) == ENULL
+    assert L.kv_page_in(P, NULL, 100, _i32(0), _i32(0), 1, P, P, 4, 128, 16, P, ws, NULL) == ENULL
+
+
+def test_resident_attention_checks():
+    # 16-token block at ctx 5000: its positions 4984..4999 lie in chunk 77 (4928..4991) and 78
+    res = lambda ids, ctx=5000, d=None: L.verify_attn_paged_resident(  # noqa: E731
+        dims() if d is None else d, P, P, P, P, _i32(*ids), len(ids), 160, ctx, 0, P, 1 << 30,
+        P, NULL, NULL)
+    assert res([]) == ETABLE                                              # nothing resident
+    assert res([0, 5, 77]) == ETABLE                                      # chunk 78 missing
+    assert res([0, 5, 78]) == ETABLE                                      # chunk 77 missing
+    assert res([0, 78, 77]) == ETABLE                                     # not increasing
+    assert res([77, 78, 79]) == ETABLE                                    # past the context
+    assert res([-1, 77, 78]) == ETABLE
+    assert L.verify_attn_paged_resident(dims(), P, P, P, P, None, 2, 160, 5000, 0, P, 1 << 30, P,
+                                        NULL, NULL) == ENULL
+    assert res([77, 78], ctx=10) == ESHAPE                                # block longer than ctx
+    assert res([77, 78], d=dims(d=96)) == ESHAPE
+    # valid lists pass the resident checks and meet the paged ones (a null slot list here)
+    assert L.verify_attn_paged_resident(dims(), P, P, P, NULL, _i32(3, 77, 78), 3, 160, 5000, 0,
+                                        P, 1 << 30, P, NULL, NULL) == ENULL
+
+
+def test_resident_workspace_is_that_of_its_chunks():
+    # the resident call splits the n_res listed chunks like a context of 64 * n_res positions:
+    # 47 chunks take 47 splits of one chunk, more than the 41 of the full 81-chunk context
+    d = dims()
+    assert L.verify_attn_paged_auto_splits(d, 64 * 47, 64) == 47
+    assert L.verify_attn_paged_auto_splits(d, 5136, 64) == 41
+    short = L.verify_attn_paged_workspace_bytes(d, 5136, 64, 0)
+    assert short < L.verify_attn_paged_workspace_bytes(d, 64 * 48, 64, 0)
+    assert L.verify_attn_paged_resident(d, P, P, P, P, _i32(*range(33, 81)), 48, 160, 5136, 0,
+                                        P, short, P, NULL, NULL) == EWS

@@ -70,3 +70,91 @@ def test_pager_argument_checks():
     assert L.rkv_pager_ctx_len(None) == -1 and L.rkv_pager_free_slots(None) == -1
     L.rkv_pager_destroy(h)
     L.rkv_pager_destroy(None)
+
+
+@pytest.mark.parametrize("seed,n_slots,n_table", [(5, 20, 80), (6, 8, 300), (7, 64, 64)])
+def test_pager_paging_matches_model(seed, n_slots, n_table):
+    """Random reserve / commit / evict / restore sequences: same slots, tables, free counts,
+    resident lists and refusals as the oracle's model."""
+    g = np.random.default_rng(seed)
+    p, m = rk.Pager(n_slots, n_table), oracle.PagerModel(n_slots, n_table)
+    for _ in range(600):
+        op = int(g.integers(0, 4))
+        if op == 0:
+            n = int(g.integers(1, 200))
+            try:
+                want = m.reserve(n)
+            except MemoryError:
+                with pytest.raises(_lib.RkvError):
+                    p.reserve(n)
+                continue
+            assert p.reserve(n) == want
+            keep = int(g.integers(0, n + 1))
+            m.commit(keep)
+            p.commit(keep)
+        elif op in (1, 2):
+            # evict: usually valid whole committed chunks, sometimes a chunk that does not qualify
+            full = m.ctx // 64
+            cand = [c for c in range(full) if m.table[c] >= 0]
+            if op == 2 or not cand:
+                bad = [int(g.integers(0, n_table))]
+                try:
+                    m.evict(bad)
+                except ValueError:
+                    with pytest.raises(_lib.RkvError) as e:
+                        p.evict(bad)
+                    assert e.value.status == EARG
+                    continue
+                assert p.evict(bad) is not None
+                continue
+            pick = [int(c) for c in g.choice(cand, size=min(len(cand), int(g.integers(1, 5))),
+                                             replace=False)]
+            assert p.evict(pick) == m.evict(pick)
+        else:
+            out = [c for c, s in enumerate(m.table) if s == oracle.PAGED_OUT]
+            if not out:
+                continue
+            pick = [int(c) for c in g.choice(out, size=min(len(out), int(g.integers(1, 6))),
+                                             replace=False)]
+            try:
+                want = m.restore(pick)
+            except MemoryError:
+                with pytest.raises(_lib.RkvError) as e:
+                    p.restore(pick)
+                assert e.value.status == ETABLE
+                continue
+            assert p.restore(pick) == want
+        assert p.table() == m.table
+        assert p.free_slots == len(m.free)
+        assert p.resident() == m.resident()
+    p.close()
+
+
+def test_pager_paging_argument_checks():
+    h = L.rkv_pager_create(4, 8)
+    first, k = ctypes.c_int32(), ctypes.c_int32()
+    slots = (ctypes.c_int32 * 17)()
+    L.rkv_pager_reserve(h, 200, ctypes.byref(first), ctypes.byref(k), slots)
+    L.rkv_pager_commit(h, 200)                                 # chunks 0..2 full, 3 partial
+    ids = (ctypes.c_int32 * 4)(3, 0, 0, 0)
+    out = (ctypes.c_int32 * 4)()
+    assert L.rkv_pager_evict(h, ids, 1, out) == EARG           # the partial tail chunk
+    ids[0] = 1
+    assert L.rkv_pager_evict(h, ids, 2, out) == OK and list(out)[:2] == [1, 0]
+    assert L.rkv_pager_evict(h, ids, 1, out) == EARG           # already out
+    ids[0], ids[1] = 2, 2
+    assert L.rkv_pager_evict(h, ids, 2, out) == EARG           # repeated
+    assert L.rkv_pager_evict(None, ids, 1, out) == ENULL
+    assert L.rkv_pager_evict(h, None, 1, out) == ENULL
+    assert L.rkv_pager_evict(h, ids, -1, out) == EARG
+    assert L.rkv_pager_evict(h, None, 0, None) == OK           # nothing to do
+    ids[0], ids[1] = 1, 0
+    assert L.rkv_pager_restore(h, ids, 2, out) == OK and list(out)[:2] == [0, 1]
+    assert L.rkv_pager_restore(h, ids, 1, out) == EARG         # resident
+    tab = (ctypes.c_int32 * 8)()
+    L.rkv_pager_table(h, tab, 8)
+    assert list(tab) == [1, 0, 2, 3, -1, -1, -1, -1]
+    assert L.rkv_pager_resident(h, None, None, 0) == 4
+    assert L.rkv_pager_resident(h, None, out, 2) == ENULL
+    assert L.rkv_pager_resident(None, None, None, 0) == ENULL
+    L.rkv_pager_destroy(h)
