@@ -10,7 +10,8 @@ data already resident in HBM; the step is captured once in a HIP graph and repla
 The JSON line also carries the per-layer figure at context 262,144 (one paged verify layer,
 both kernels), the roofline of the dominant kernel (the paged split-K attention kernel, timed
 live with HIP events on the stream it runs on), the step by layer type, 1,024-token prefill
-blocks through the pool and the ring (with their own matrix-core roofline), the four single-layer
+blocks through the pool and the ring (with their own matrix-core roofline), host paging of
+chunks over PCIe and the verify over 8K resident of 256K, the four single-layer
 workloads timed one by one (cold and warm, median / p10 / p90), a measured HBM read bandwidth,
 and the fp64 oracle timed on the host cores over a bounded sample of the same workload (plus one
 call per single-layer workload).
@@ -19,8 +20,9 @@ call per single-layer workload).
     python bench.py --mode copy     # plain 1-GiB device copies, for HBM counter calibration
     python bench.py --mode kernel   # the dominant kernel alone (10 launches), for counter runs
     python bench.py --mode configs  # each single-layer workload and block append called 100
-                                    # times (30 at 256K and for the prefill blocks), a
-                                    # cache-evicting read before each, for a kernel trace
+                                    # times (30 at 256K, for the prefill blocks and for a page-out
+                                    # and page-in of 128 chunks), a cache-evicting read before
+                                    # each, for a kernel trace
     python bench.py --mode traffic --fetch F.csv --write W.csv --copy-fetch CF.csv --copy-write CW.csv
                                     # HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE /
                                     # WRITE_SIZE counter files, scaled by the copy calibration
@@ -65,6 +67,8 @@ def parse():
                     help="skip the single-layer workloads timed one by one")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the 1,024-token prefill blocks")
+    ap.add_argument("--no-paging", action="store_true",
+                    help="skip host paging and the resident-subset verify")
     return ap.parse_args()
 
 
@@ -369,6 +373,15 @@ def config_calls(torch, rk, synth, probe, n_small, n_large):
             run(lambda: rk.verify_attn_paged(q, kp, vp, pt, c.ctx_len, out=o, lse=l), n_large)
             del kp, vp
         torch.cuda.empty_cache()
+    # host paging: 128 chunks out to pinned host memory and back, one run of chunk ids
+    kp = torch.zeros((1024, 4, 64, 128), dtype=torch.bfloat16, device="cuda")
+    vp = torch.zeros((1024, 4, 128, 64), dtype=torch.bfloat16, device="cuda")
+    kh = torch.empty((1024, 4, 64, 128), dtype=torch.bfloat16, pin_memory=True)
+    vh = torch.empty((1024, 4, 128, 64), dtype=torch.bfloat16, pin_memory=True)
+    slots, ids = list(range(512, 640)), list(range(200, 328))
+    ws = rk.kv_page_out(kp, vp, slots, ids, kh, vh)
+    run(lambda: rk.kv_page_out(kp, vp, slots, ids, kh, vh, workspace=ws), n_large)
+    run(lambda: rk.kv_page_in(kh, vh, ids, slots, kp, vp, workspace=ws), n_large)
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, vendor figure
@@ -432,6 +445,65 @@ def prefill_timings(torch, rk, synth, reps):
         "us": round(stack_us, 1), "tokens_per_s": round(1024 / (stack_us * 1e-6)),
         "note": "attention only (30 ring layers + 10 paged layers at 131,072) of one 1,024-token "
                 "prefill block; the pages' ~3,500 tok/s is whole-engine prefill on an RTX 3090"}
+    return out
+
+
+PCIE_PEAK_GBPS = 64.0   # PCIe 5.0 x16, one direction, vendor figure
+
+
+def paging_timings(torch, rk, reps):
+    """Host paging: 128 chunks (8,192 positions, 4 KV heads, D 128: 16 MiB of K and V) paged out
+    to pinned host memory and back in, as one run of consecutive chunk ids and as 128 scattered
+    ones (µs per call, events around `reps` eager calls); and the pages' own configuration, a
+    verify block at context 262,144 with 8,192 positions resident (128 drawn chunks + the block's
+    own), attention over the resident subset in graph replay."""
+    g = torch.Generator(device="cuda").manual_seed(7)
+    n, n_slots, n_host, hkv, d = 128, 1024, 1024, 4, 128
+    kp = torch.randn((n_slots, hkv, 64, d), device="cuda", generator=g).to(torch.bfloat16)
+    vp = torch.randn((n_slots, hkv, d, 64), device="cuda", generator=g).to(torch.bfloat16)
+    kh = torch.empty((n_host, hkv, 64, d), dtype=torch.bfloat16, pin_memory=True)
+    vh = torch.empty((n_host, hkv, d, 64), dtype=torch.bfloat16, pin_memory=True)
+    perm = torch.randperm(n_slots, generator=torch.Generator().manual_seed(8)).tolist()
+    slots = perm[:n]
+    runs = {"one_run": list(range(200, 200 + n)),
+            "scattered": sorted(torch.randperm(n_host, generator=torch.Generator().manual_seed(9))
+                                [:n].tolist())}
+    nbytes = n * 2 * hkv * 64 * d * 2
+    ws = rk.kv_page_out(kp, vp, slots, runs["one_run"], kh, vh)
+    out = {"chunks": n, "bytes": nbytes, "pcie_peak_gbps": PCIE_PEAK_GBPS}
+    for name, ids in runs.items():
+        for way in ("out", "in"):
+            if way == "out":
+                fn = lambda ids=ids: rk.kv_page_out(kp, vp, slots, ids, kh, vh, workspace=ws)  # noqa: E731
+            else:
+                fn = lambda ids=ids: rk.kv_page_in(kh, vh, ids, slots, kp, vp, workspace=ws)  # noqa: E731
+            for _ in range(3):
+                fn()
+            # median of three rounds (the first copies to a fresh pinned buffer in a process
+            # can take several times longer)
+            us = sorted(event_ms(fn, reps, torch) for _ in range(3))[1] * 1e3
+            gbps = nbytes / (us * 1e-6) / 1e9
+            out[f"page_{way}_{name}"] = {"us": round(us, 1), "gbps": round(gbps, 2),
+                                          "pcie_frac": round(gbps / PCIE_PEAK_GBPS, 4)}
+    del kp, vp, kh, vh, ws
+    torch.cuda.empty_cache()
+    # verify at 262,144 with 8K resident: 128 drawn chunks below the block's + chunk 4,095
+    gen = torch.Generator().manual_seed(10)
+    ids = sorted(torch.randperm(4095, generator=gen)[:128].tolist()) + [4095]
+    n_res = len(ids)
+    kp = torch.randn((n_res, hkv, 64, d), device="cuda", generator=g).to(torch.bfloat16)
+    vp = torch.randn((n_res, hkv, d, 64), device="cuda", generator=g).to(torch.bfloat16)
+    q = torch.randn((16, 16, d), device="cuda", generator=g).to(torch.bfloat16)
+    d_slots = torch.arange(n_res, dtype=torch.int32, device="cuda")
+    o = torch.empty((16, 16, d), dtype=torch.float32, device="cuda")
+    l = torch.empty((16, 16), dtype=torch.float32, device="cuda")
+    fn = lambda: rk.verify_attn_paged_resident(q, kp, vp, d_slots, ids, 262144, out=o, lse=l)  # noqa: E731
+    us = graph_ms(fn, 20, reps, torch) * 1e3
+    kv = n_res * 2 * hkv * 64 * d * 2
+    out["verify_256k_8k_resident"] = {"us": round(us, 2), "resident_chunks": n_res,
+                                      "kv_bytes": kv, "gbps": round(kv / (us * 1e-6) / 1e9, 1),
+                                      "note": "the pages' configuration: 8K of the 256K context "
+                                              "resident; graph replay, back to back"}
     return out
 
 
@@ -769,6 +841,10 @@ def main():
     if not args.no_prefill:
         log("batched prefill blocks")
         res["prefill_gpu"] = prefill_timings(torch, rk, synth, max(3, args.steps // 4))
+
+    if not args.no_paging:
+        log("host paging")
+        res["paging_gpu"] = paging_timings(torch, rk, max(5, args.steps // 2))
 
     if not args.no_configs:
         log("single-layer workloads, cold and warm")

@@ -303,12 +303,15 @@ int32_t verify_kv_append_paged(const void* k_new, const void* v_new, int32_t n,
  *   kv_page_out  pool slot slots[i] -> host entry chunk_ids[i], i < n (K and V, bit-exact)
  *   kv_page_in   host entry chunk_ids[i] -> pool slot slots[i]
  * slots and chunk_ids are host arrays, read before the call returns; chunk ids must be
- * distinct in a page-out and slots distinct in a page-in.  Both calls go through a device
- * workspace of kv_page_workspace_bytes(n_kv_heads, head_dim, n) bytes: a kernel packs the
- * chunks there (or unpacks them), and they cross PCIe with one copy per run of consecutive
- * chunk ids, RKV_PAGE_BATCH chunks at a time.  Both are asynchronous on `stream`: the host
- * entries (page-out) or the slots (page-in) hold the data once the stream has passed the
- * call, and a slot freed by a page-out may be rewritten by any later work on that stream.
+ * distinct in a page-out and slots distinct in a page-in.  RKV_PAGE_BATCH chunks at a time
+ * cross PCIe one of two ways: when the host store is pinned memory the device can address, a
+ * kernel copies each chunk straight between its slot and its host entry (every page-out, and
+ * page-ins of scattered chunk ids); otherwise a kernel packs the chunks into a device
+ * workspace and the copy engines move one copy per run of consecutive chunk ids.  Pass a
+ * workspace of kv_page_workspace_bytes(n_kv_heads, head_dim, n) bytes either way.  Both
+ * calls are asynchronous on `stream`: the host entries (page-out) or the slots (page-in) hold
+ * the data once the stream has passed the call, and a slot freed by a page-out may be
+ * rewritten by any later work on that stream.
  * Status: RKV_ERR_NULL; RKV_ERR_SHAPE (head counts, head_dim); RKV_ERR_ARG (n < 0, a chunk id
  * outside [0, n_host), a repeated chunk id or slot); RKV_ERR_TABLE (a slot outside
  * [0, n_slots)); RKV_ERR_WORKSPACE; RKV_ERR_HIP.

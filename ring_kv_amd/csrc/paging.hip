@@ -3,10 +3,14 @@
 // 256K context", "Three optimizations", item 1: cold chunks page to host RAM).
 //
 // A chunk's K and V are each one contiguous block of n_kv_heads * 64 * head_dim bf16 in a slot,
-// so the copies need no layout change.  The slots of a batch are scattered over the pool and the
-// host entries follow the chunk ids, so the chunks are packed into a device staging area by a
-// kernel (HBM to HBM) and cross PCIe with the copy engines, one copy per run of consecutive chunk
-// ids; no kernel touches host memory.
+// so the copies need no layout change.  Two paths, chosen per batch:
+//  * long runs of consecutive chunk ids, or a store the device cannot address: the chunks are
+//    packed into a device staging area by a kernel (HBM to HBM) and cross PCIe with the copy
+//    engines, one copy per run;
+//  * a pinned host store, for every page-out and for page-ins of scattered chunk ids (where one
+//    copy per run would pay the copy engines' per-copy cost many times): a kernel copies every
+//    chunk straight between its slot and its host entry, through the address the runtime maps
+//    for the device (hipHostGetDevicePointer; memory it cannot map always takes the first path).
 #include <algorithm>
 #include <vector>
 
@@ -34,7 +38,40 @@ __global__ __launch_bounds__(kPageThreads) void page_copy_kernel(PageArgs a) {
     dst[u] = src[u];
 }
 
+// Entry e < n is the K block of chunk e, entry n + e its V block, copied between pool slot
+// slots[e] and host entry chunk_ids[e].  Each thread keeps kUnroll 16-byte loads in flight before
+// its stores: reads across PCIe take microseconds, and only many requests in flight fill the link.
+constexpr int kUnroll = 4;
+__global__ __launch_bounds__(kPageThreads) void page_host_kernel(PageHostArgs a) {
+  const int e = blockIdx.x;
+  const int i = e % a.n;
+  const bool v = e >= a.n;
+  uint8_t* pool = (v ? a.pool_v : a.pool_k) + (int64_t)a.slots[i] * a.chunk_bytes;
+  uint8_t* host = (v ? a.host_v : a.host_k) + (int64_t)a.chunk_ids[i] * a.chunk_bytes;
+  const u32x4* src = reinterpret_cast<const u32x4*>(a.to_host ? pool : host);
+  u32x4* dst = reinterpret_cast<u32x4*>(a.to_host ? host : pool);
+  const int64_t n16 = a.chunk_bytes / 16;
+  const int64_t step = (int64_t)gridDim.y * kPageThreads;
+  for (int64_t u0 = (int64_t)blockIdx.y * kPageThreads + threadIdx.x; u0 < n16;
+       u0 += step * kUnroll) {
+    u32x4 r[kUnroll];
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k)
+      if (u0 + k * step < n16) r[k] = src[u0 + k * step];
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k)
+      if (u0 + k * step < n16) dst[u0 + k * step] = r[k];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_page_host(const PageHostArgs& a, hipStream_t stream) {
+  const int64_t n16 = a.chunk_bytes / 16;
+  const int parts = (int)std::min<int64_t>(8, (n16 + kPageThreads - 1) / kPageThreads);
+  hipLaunchKernelGGL(page_host_kernel, dim3(2 * a.n, parts), dim3(kPageThreads), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_page_copy(const PageArgs& a, hipStream_t stream) {
   const int64_t n16 = a.chunk_bytes / 16;
@@ -106,6 +143,53 @@ hipError_t copy_runs(const int32_t* chunk_ids, int32_t b0, int32_t b1, uint8_t* 
   return hipSuccess;
 }
 
+// Runs of consecutive chunk ids in batch [b0, b1).
+int32_t count_runs(const int32_t* chunk_ids, int32_t b0, int32_t b1) {
+  int32_t runs = 1;
+  for (int32_t i = b0 + 1; i < b1; ++i) runs += chunk_ids[i] != chunk_ids[i - 1] + 1;
+  return runs;
+}
+
+// With a host store the device can address (pinned memory), a page-out always takes the direct
+// kernel (measured: 310 µs for 128 chunks in one run against 327 µs through staging and the copy
+// engines, the same for scattered ids), and a page-in takes it for scattered ids (runs shorter
+// than kMinRun chunks on average: 353 µs for 128 scattered chunks against ~2.5 ms for one copy
+// per run); a page-in of long runs goes through the copy engines (329 µs against 357 µs).
+constexpr int32_t kMinRun = 8;
+
+// Device-visible addresses of the two host stores, or false when either is not pinned memory
+// mapped for the device (then only the copy engines touch it).
+bool host_device_ptrs(const void* k_host, const void* v_host, uint8_t** dk, uint8_t** dv) {
+  void* a = nullptr;
+  void* b = nullptr;
+  if (hipHostGetDevicePointer(&a, const_cast<void*>(k_host), 0) != hipSuccess ||
+      hipHostGetDevicePointer(&b, const_cast<void*>(v_host), 0) != hipSuccess) {
+    (void)hipGetLastError();   // the query failed; leave no error for the next call to report
+    return false;
+  }
+  *dk = static_cast<uint8_t*>(a);
+  *dv = static_cast<uint8_t*>(b);
+  return true;
+}
+
+hipError_t direct_batch(void* k_pool, void* v_pool, uint8_t* dk, uint8_t* dv, int64_t cb,
+                        const int32_t* slots, const int32_t* chunk_ids, int32_t b0, int32_t b1,
+                        bool to_host, hipStream_t st) {
+  rkv::PageHostArgs a{};
+  a.pool_k = static_cast<uint8_t*>(k_pool);
+  a.pool_v = static_cast<uint8_t*>(v_pool);
+  a.host_k = dk;
+  a.host_v = dv;
+  a.chunk_bytes = cb;
+  a.n = b1 - b0;
+  a.to_host = to_host ? 1 : 0;
+  for (int32_t i = b0; i < b1; ++i) {
+    a.slots[i - b0] = slots[i];
+    a.chunk_ids[i - b0] = chunk_ids[i];
+  }
+  return rkv::launch_page_host(a, st);
+}
+
 rkv::PageArgs batch_args(void* k_pool, void* v_pool, void* workspace, int64_t cb,
                          const int32_t* slots, int32_t b0, int32_t b1, bool to_stage) {
   rkv::PageArgs a{};
@@ -140,8 +224,16 @@ int32_t kv_page_out(const void* k_pool, const void* v_pool, int32_t n_kv_heads,
   if (st != RKV_OK || n == 0) return st;
   const int64_t cb = chunk_bytes_of(n_kv_heads, head_dim);
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  uint8_t *dk = nullptr, *dv = nullptr;
+  const bool direct_ok = host_device_ptrs(k_host, v_host, &dk, &dv);
   for (int32_t b0 = 0; b0 < n; b0 += RKV_PAGE_BATCH) {
     const int32_t b1 = std::min<int32_t>(n, b0 + RKV_PAGE_BATCH);
+    if (direct_ok) {
+      if (direct_batch(const_cast<void*>(k_pool), const_cast<void*>(v_pool), dk, dv, cb, slots,
+                       chunk_ids, b0, b1, true, hs) != hipSuccess)
+        return RKV_ERR_HIP;
+      continue;
+    }
     rkv::PageArgs a = batch_args(const_cast<void*>(k_pool), const_cast<void*>(v_pool), workspace,
                                  cb, slots, b0, b1, true);
     hipError_t e = rkv::launch_page_copy(a, hs);
@@ -164,8 +256,16 @@ int32_t kv_page_in(const void* k_host, const void* v_host, int64_t n_host,
   if (st != RKV_OK || n == 0) return st;
   const int64_t cb = chunk_bytes_of(n_kv_heads, head_dim);
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  uint8_t *dk = nullptr, *dv = nullptr;
+  const bool direct_ok = host_device_ptrs(k_host, v_host, &dk, &dv);
   for (int32_t b0 = 0; b0 < n; b0 += RKV_PAGE_BATCH) {
     const int32_t b1 = std::min<int32_t>(n, b0 + RKV_PAGE_BATCH);
+    if (direct_ok && count_runs(chunk_ids, b0, b1) * kMinRun > b1 - b0) {
+      if (direct_batch(k_pool, v_pool, dk, dv, cb, slots, chunk_ids, b0, b1, false, hs) !=
+          hipSuccess)
+        return RKV_ERR_HIP;
+      continue;
+    }
     hipError_t e = copy_runs(chunk_ids, b0, b1, static_cast<uint8_t*>(workspace),
                              static_cast<uint8_t*>(const_cast<void*>(k_host)),
                              static_cast<uint8_t*>(const_cast<void*>(v_host)), cb, false, hs);

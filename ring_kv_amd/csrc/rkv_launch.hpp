@@ -118,4 +118,19 @@ struct PageArgs {
 };
 hipError_t launch_page_copy(const PageArgs& a, hipStream_t stream);
 
+// Whole chunks straight between pool slots and host entries, through the device-visible address
+// of pinned host memory (for batches whose chunk ids are scattered).
+struct PageHostArgs {
+  uint8_t* pool_k;
+  uint8_t* pool_v;
+  uint8_t* host_k;        // device-visible address of the host store's entry 0
+  uint8_t* host_v;
+  int64_t chunk_bytes;
+  int32_t n;
+  int32_t to_host;        // 1: pool -> host, 0: host -> pool
+  int32_t slots[RKV_PAGE_BATCH];
+  int32_t chunk_ids[RKV_PAGE_BATCH];
+};
+hipError_t launch_page_host(const PageHostArgs& a, hipStream_t stream);
+
 }  // namespace rkv

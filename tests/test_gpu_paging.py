@@ -28,17 +28,27 @@ def _pinned(shape):
     return torch.zeros(shape, dtype=torch.bfloat16, pin_memory=True)
 
 
-def test_page_out_in_round_trip_bit_exact():
+@pytest.mark.parametrize("pattern,pinned", [("runs", True), ("mixed", True), ("scattered", True),
+                                            ("scattered", False)])
+def test_page_out_in_round_trip_bit_exact(pattern, pinned):
+    """300 chunks (two batches) out to a host store and back into other slots: long runs of chunk
+    ids go through the copy engines, scattered ids through the direct kernel (pinned stores) or
+    one copy per run (a pageable store)."""
     g = np.random.default_rng(61)
     n_slots, hkv, d, n_host = 400, 4, 128, 500
     kp, vp = _bits(g, (n_slots, hkv, CH, d)), _bits(g, (n_slots, hkv, d, CH))
     kd, vd = dev(kp), dev(vp)
-    kh, vh = _pinned((n_host, hkv, CH, d)), _pinned((n_host, hkv, d, CH))
-    # 300 chunks (two batches): runs of consecutive chunk ids and scattered ones
-    ids = list(range(10, 150)) + list(range(300, 380)) + [int(c) for c in
-                                                          g.choice(np.arange(400, 500), 80, replace=False)]
+    make = _pinned if pinned else (lambda sh: torch.zeros(sh, dtype=torch.bfloat16))
+    kh, vh = make((n_host, hkv, CH, d)), make((n_host, hkv, d, CH))
+    if pattern == "runs":
+        ids = list(range(10, 160)) + list(range(300, 450))
+    elif pattern == "mixed":
+        ids = list(range(10, 150)) + list(range(300, 380)) + \
+            [int(c) for c in g.choice(np.arange(400, 500), 80, replace=False)]
+    else:
+        ids = [int(c) for c in g.choice(n_host, 300, replace=False)]
     slots = [int(s) for s in g.permutation(n_slots)[:len(ids)]]
-    say(f"page out {len(ids)} chunks")
+    say(f"page out {len(ids)} chunks ({pattern}, {'pinned' if pinned else 'pageable'})")
     rk.kv_page_out(kd, vd, slots, ids, kh, vh)
     torch.cuda.synchronize()
     khn, vhn = _host(kh), _host(vh)
