@@ -379,7 +379,8 @@ def config_calls(torch, rk, synth, probe, n_small, n_large):
     kh = torch.empty((1024, 4, 64, 128), dtype=torch.bfloat16, pin_memory=True)
     vh = torch.empty((1024, 4, 128, 64), dtype=torch.bfloat16, pin_memory=True)
     slots, ids = list(range(512, 640)), list(range(200, 328))
-    ws = rk.kv_page_out(kp, vp, slots, ids, kh, vh)
+    ws = torch.empty(rk.lib().kv_page_workspace_bytes(4, 128, 128), dtype=torch.uint8,
+                     device="cuda")
     run(lambda: rk.kv_page_out(kp, vp, slots, ids, kh, vh, workspace=ws), n_large)
     run(lambda: rk.kv_page_in(kh, vh, ids, slots, kp, vp, workspace=ws), n_large)
 
