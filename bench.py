@@ -19,6 +19,7 @@ call per single-layer workload).
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload stack_40l_131k|paged_256k]
     python bench.py --mode copy     # plain 1-GiB device copies, for HBM counter calibration
     python bench.py --mode kernel   # the dominant kernel alone (10 launches), for counter runs
+    python bench.py --mode prefill-kernel   # the prefill kernel alone at 131,072 (3 launches)
     python bench.py --mode configs  # each single-layer workload and block append called 100
                                     # times (30 at 256K, for the prefill blocks and for a page-out
                                     # and page-in of 128 chunks), a cache-evicting read before
@@ -57,7 +58,7 @@ def parse():
     ap.add_argument("--workload", default="stack_40l_131k",
                     choices=["stack_40l_131k", "paged_256k"])
     ap.add_argument("--mode", default="bench",
-                    choices=["bench", "copy", "kernel", "traffic", "configs"])
+                    choices=["bench", "copy", "kernel", "prefill-kernel", "traffic", "configs"])
     for f in ("fetch", "write", "copy_fetch", "copy_write"):
         ap.add_argument("--" + f.replace("_", "-"), default=None)
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
@@ -707,6 +708,20 @@ def main():
             rk.verify_attn_paged_partial(q, kp, vp, pt, 131072, splits, part_out=po, part_lse=pl)
         torch.cuda.synchronize()
         print(json.dumps({"mode": "kernel", "launches": 10, "splits": splits}), flush=True)
+        return
+
+    if args.mode == "prefill-kernel":
+        # the prefill kernel alone: 3 launches over the 1,024-token block ending at 131,072,
+        # 4 splits (partials, no merge)
+        c, _ = synth.workload("prefill_pool_131k", keep_rows=False)
+        t = lambda a: rk.tensor_from_numpy(a, "cuda")  # noqa: E731
+        q, kp, vp, pt = t(c.q), t(c.k_pool), t(c.v_pool), t(c.page_table)
+        po = torch.empty((4, 4, 4096, 128), dtype=torch.float32, device="cuda")
+        pl = torch.empty((4, 4, 4096), dtype=torch.float32, device="cuda")
+        for _ in range(3):
+            rk.verify_attn_paged_partial(q, kp, vp, pt, c.ctx_len, 4, part_out=po, part_lse=pl)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "prefill-kernel", "launches": 3, "splits": 4}), flush=True)
         return
 
     if args.mode == "configs":
