@@ -8,11 +8,16 @@
 // arithmetic per key and is bound by the matrix cores, so the tiling favours reuse of every
 // K/V element staged in LDS:
 //
-//   workgroup = one KV head g, one split (range of whole chunks), one tile of 32*NW rows; each of
-//   its NW waves owns 32 rows and computes, per 64-key chunk,
+//   workgroup = one KV head g, one split (range of whole chunks), one tile of 32*NRG rows in 8
+//   waves; each wave owns 32 rows and computes, per 64-key chunk (KS = 1) or per 32-key half of
+//   it (KS = 2: two waves per row group, one per half),
 //     S^T [64 keys x 32 rows] = K [64 x D] . Q^T          2 x (D/16) MFMA 32x32x16 bf16
 //     online softmax of each row over the chunk's keys  (f32, exp2 domain)
 //     O^T [D x 32 rows]     += V^T [D x 64] . P^T         (D/32) x 4 MFMA 32x32x16 bf16
+//   (half of each with KS = 2, whose two halves merge their softmax states at the end).
+//   256-row tiles give every K/V element staged in LDS the most reuse; 128-row tiles (KS = 2)
+//   double the workgroups of a block whose 256-row grid leaves most of the chip idle (a block
+//   over the ring, where each tile sees only its window and is not split).
 //
 // S is computed transposed so that each lane ends with 16 scores of ONE row per 32-key tile,
 // which after a fixed permutation of the keys (rho below) is exactly the B operand of P^T for
@@ -93,22 +98,27 @@ struct PTile {
   }
 };
 
-template <int D, int NW, bool PAGED>
-__global__ __launch_bounds__(NW * 64, 2)
+template <int D, int NRG, int KS, bool PAGED>
+__global__ __launch_bounds__(NRG * KS * 64, 2)
 void prefill_attn_kernel(ChunkAttnArgs a) {
   using T = PTile<D>;
+  constexpr int NW = NRG * KS;
   constexpr int NT = NW * 64;
-  constexpr int ROWS = 32 * NW;
+  constexpr int ROWS = 32 * NRG;
+  constexpr int NKT = KS == 2 ? 1 : 2;    // 32-key tiles per chunk computed by one wave
   constexpr int LPC = (T::kPieces + T::vPieces) / NT;   // 16-byte loads per chunk per thread
   static_assert((T::kPieces + T::vPieces) % NT == 0 && T::kPieces % NT == 0, "piece split");
   constexpr int KK = D / 16;    // 16-dim steps of S^T
   constexpr int DT = D / 32;    // 32-dim tiles of O^T
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][T::elems];
+  __shared__ float xstate[KS == 2 ? NRG * 3 * 64 : 1];   // key half 1's m, l_run, l_rnd per lane
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = w % NRG;                 // row group: rows 32rg .. 32rg+31 of the tile
+  const int kh = w / NRG;                 // key half (KS = 2): keys 32kh .. 32kh+31 of a chunk
   const int n = lane & 31;
   const int h = lane >> 5;
 
@@ -137,7 +147,7 @@ void prefill_attn_kernel(ChunkAttnArgs a) {
   const int nloc = (int)imax64(0, c_to - c_from);
 
   // ---- this lane's row -------------------------------------------------------------------------
-  const int r = row0 + 32 * w + n;
+  const int r = row0 + 32 * rg + n;
   const bool row_ok = r < rows;
   const int qi = row_ok ? r / G : 0;
   const int hq = g * G + (row_ok ? r % G : 0);
@@ -231,22 +241,24 @@ void prefill_attn_kernel(ChunkAttnArgs a) {
     for (int v = 0; v < 16; ++v) oacc[t][v] = 0.f;
   const float csc = a.scale_log2;
 
-  // Per chunk: S^T of both 32-key tiles first, then tile by tile the softmax and its half of
-  // the PV product.  The order lets the matrix core run tile 1's QK products while the vector
-  // unit works on tile 0's scores, and tile 0's PV products while it works on tile 1's.
+  // Per chunk (KS = 1): S^T of both 32-key tiles first, then tile by tile the softmax and its
+  // half of the PV product.  The order lets the matrix core run tile 1's QK products while the
+  // vector unit works on tile 0's scores, and tile 0's PV products while it works on tile 1's.
+  // With KS = 2 a wave computes only tile kh and the two waves of a SIMD overlap instead.
   auto compute = [&](const uint16_t* buf, int loc, bool ok, auto edge_tag) __attribute__((always_inline)) {
     constexpr bool EDGE = decltype(edge_tag)::value;
     const int cbase = loc * 64;
-    f32x16 sacc[2];
+    f32x16 sacc[NKT];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int j = 0; j < NKT; ++j) {
+      const int kt = KS == 2 ? kh : j;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) sacc[kt][v] = 0.f;
+      for (int v = 0; v < 16; ++v) sacc[j][v] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         const bf16x8 ka =
             *reinterpret_cast<const bf16x8*>(buf + T::k_off(rho(kt, n), 2 * kk + h));
-        sacc[kt] = mfma_32x32x16(ka, qop[kk], sacc[kt]);
+        sacc[j] = mfma_32x32x16(ka, qop[kk], sacc[j]);
       }
     }
     // visible keys of this row relative to the chunk, and the V words of keys without a stored
@@ -259,15 +271,17 @@ void prefill_attn_kernel(ChunkAttnArgs a) {
       vzero = !ok || cbase < vlo || cbase + 64 > vhi;
     }
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int j = 0; j < NKT; ++j) {
+      const int kt = KS == 2 ? kh : j;
       // item v of tile kt is key 32kt + 16(v/8) + 8h + v%8 of the chunk
       if constexpr (EDGE) {
-        // key - 8h is a compile-time constant per item: compare it with the bounds shifted by 8h
-        const int lo8 = vis_lo - 8 * h, hi8 = vis_hi - 8 * h;
+        // key - 32kt - 8h is a compile-time constant per item: compare it with the bounds
+        // shifted by 32kt + 8h
+        const int lo8 = vis_lo - 32 * kt - 8 * h, hi8 = vis_hi - 32 * kt - 8 * h;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int kc = 32 * kt + 16 * (v >> 3) + (v & 7);
-          if (kc < lo8 || kc > hi8) sacc[kt][v] = -INFINITY;   // select, not arithmetic
+          const int kc = 16 * (v >> 3) + (v & 7);
+          if (kc < lo8 || kc > hi8) sacc[j][v] = -INFINITY;    // select, not arithmetic
         }
       }
       // Weights against the row's current reference m_use (0 before the row has one); the max
@@ -278,7 +292,7 @@ void prefill_attn_kernel(ChunkAttnArgs a) {
       const float m_use = m_run == -INFINITY ? 0.f : m_run;
       float pv[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) pv[v] = __builtin_amdgcn_exp2f(fmaf(sacc[kt][v], csc, -m_use));
+      for (int v = 0; v < 16; ++v) pv[v] = __builtin_amdgcn_exp2f(fmaf(sacc[j][v], csc, -m_use));
       float pm = pv[0];
 #pragma unroll
       for (int v = 1; v < 16; ++v) pm = fmaxf(pm, pv[v]);
@@ -287,9 +301,9 @@ void prefill_attn_kernel(ChunkAttnArgs a) {
       if (__builtin_amdgcn_ballot_w64(grow)) {
         // the empty volatile asm keeps the compiler from executing this path unconditionally
         asm volatile("" ::);
-        float mx = sacc[kt][0];
+        float mx = sacc[j][0];
 #pragma unroll
-        for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sacc[kt][v]);
+        for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sacc[j][v]);
         const float t_max = pair_max(mx) * csc;
         const float m_new = (grow && t_max != -INFINITY) ? t_max : m_use;
         const float alpha = (grow && m_run != -INFINITY) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
@@ -298,7 +312,7 @@ void prefill_attn_kernel(ChunkAttnArgs a) {
         l_run *= alpha;
         l_rnd *= alpha;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) pv[v] = __builtin_amdgcn_exp2f(fmaf(sacc[kt][v], csc, -m_new));
+        for (int v = 0; v < 16; ++v) pv[v] = __builtin_amdgcn_exp2f(fmaf(sacc[j][v], csc, -m_new));
         m_run = (grow && t_max == -INFINITY) ? m_run : m_new;
       } else {
         m_run = m_use;
@@ -322,11 +336,12 @@ void prefill_attn_kernel(ChunkAttnArgs a) {
         uint32_t vmask[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
         if constexpr (EDGE) {
           if (vzero) {
-            // key cbase + 16kb + 8h + e is stored iff 16kb + e lies in [slo, shi)
-            const int slo = ok ? vlo - cbase - 8 * h : 64, shi = vhi - cbase - 8 * h;
+            // key cbase + 16kb + 8h + e is stored iff 16hb + e lies in [slo, shi)
+            const int slo = ok ? vlo - cbase - 32 * kt - 8 * h : 64;
+            const int shi = vhi - cbase - 32 * kt - 8 * h;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const int kc = 16 * kb + e;
+              const int kc = 16 * hb + e;
               if (kc < slo || kc >= shi) vmask[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
             }
           }
@@ -383,6 +398,48 @@ void prefill_attn_kernel(ChunkAttnArgs a) {
   }
 
   // ---- epilogue ---------------------------------------------------------------------------------
+  if constexpr (KS == 2) {
+    // Key half 1 hands its state to key half 0 through the idle LDS tiles (32 rows x D floats per
+    // row group: exactly the two tiles); row n's 16-byte pieces are XOR-swizzled by n so that a
+    // wave's 32 rows spread over all banks.  Both states are relative to their own reference
+    // max; a half that saw no visible key has m = -inf and weighs nothing.
+    static_assert(NRG * 32 * D * 4 <= 2 * T::elems * 2, "exchange fits the tiles");
+    float* xo = reinterpret_cast<float*>(&lds[0][0]);
+    auto xo_off = [&](int t, int j) __attribute__((always_inline)) {
+      const int piece = 8 * t + 2 * j + h;                 // dims 32t + 8j + 4h .. +3
+      return (rg * 32 + n) * D + ((piece ^ (n & (D / 4 - 1))) << 2);
+    };
+    lds_barrier();                                         // every wave is done with the tiles
+    if (kh == 1) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<f32x4*>(&xo[xo_off(t, j)]) =
+              f32x4{oacc[t][4 * j], oacc[t][4 * j + 1], oacc[t][4 * j + 2], oacc[t][4 * j + 3]};
+      xstate[(rg * 3 + 0) * 64 + lane] = m_run;
+      xstate[(rg * 3 + 1) * 64 + lane] = l_run;
+      xstate[(rg * 3 + 2) * 64 + lane] = l_rnd;
+    }
+    lds_barrier();
+    if (kh == 1) return;
+    const float m1 = xstate[(rg * 3 + 0) * 64 + lane];
+    const float M = fmaxf(m_run, m1);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    const float a0 = __builtin_amdgcn_exp2f(m_run - Mu);    // -inf -> 0
+    const float a1 = __builtin_amdgcn_exp2f(m1 - Mu);
+    l_run = l_run * a0 + xstate[(rg * 3 + 1) * 64 + lane] * a1;
+    l_rnd = l_rnd * a0 + xstate[(rg * 3 + 2) * 64 + lane] * a1;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 o1 = *reinterpret_cast<const f32x4*>(&xo[xo_off(t, j)]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) oacc[t][4 * j + e] = oacc[t][4 * j + e] * a0 + o1[e] * a1;
+      }
+    m_run = M;
+  }
   if (!row_ok) return;
   const float l = pair_sum(l_run);
   const float lr = pair_sum(l_rnd);
@@ -408,17 +465,24 @@ void prefill_attn_kernel(ChunkAttnArgs a) {
     }
 }
 
+template <int D, int NRG, int KS>
+hipError_t launch_t(const ChunkAttnArgs& a, hipStream_t stream) {
+  const int rows = a.q_len * a.G;
+  const int tiles = (rows + 32 * NRG - 1) / (32 * NRG);
+  const dim3 blocks(a.n_kv_heads * a.num_splits * tiles);
+  const dim3 threads(NRG * KS * 64);
+  if (a.pt != nullptr)
+    hipLaunchKernelGGL((prefill_attn_kernel<D, NRG, KS, true>), blocks, threads, 0, stream, a);
+  else
+    hipLaunchKernelGGL((prefill_attn_kernel<D, NRG, KS, false>), blocks, threads, 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_d(const ChunkAttnArgs& a, hipStream_t stream) {
-  constexpr int NW = kPrefillTileRows / 32;
-  const int rows = a.q_len * a.G;
-  const int tiles = (rows + kPrefillTileRows - 1) / kPrefillTileRows;
-  const dim3 blocks(a.n_kv_heads * a.num_splits * tiles);
-  if (a.pt != nullptr)
-    hipLaunchKernelGGL((prefill_attn_kernel<D, NW, true>), blocks, dim3(NW * 64), 0, stream, a);
-  else
-    hipLaunchKernelGGL((prefill_attn_kernel<D, NW, false>), blocks, dim3(NW * 64), 0, stream, a);
-  return hipGetLastError();
+  if (prefill_tile_rows(a.q_len * a.G, a.n_kv_heads, a.num_splits) == kPrefillTileRows)
+    return launch_t<D, kPrefillTileRows / 32, 1>(a, stream);
+  return launch_t<D, kPrefillTileRows / 64, 2>(a, stream);
 }
 
 }  // namespace

@@ -39,6 +39,15 @@ struct ChunkAttnArgs {
 // kernel with tiles of kPrefillTileRows rows.  launch_chunk_attn picks the kernel.
 constexpr int kVerifyMaxRows = 256;
 constexpr int kPrefillTileRows = 256;
+// Row tile of the prefill kernel: kPrefillTileRows, or half of it (two waves per row group, one
+// per half of each chunk's keys) when the full tiles would leave most of the chip without a
+// workgroup (fewer than kPrefillFillWorkgroups).
+constexpr int kPrefillFillWorkgroups = 256;
+inline int prefill_tile_rows(int rows, int n_kv_heads, int num_splits) {
+  const int64_t full = (int64_t)n_kv_heads * num_splits *
+                       ((rows + kPrefillTileRows - 1) / kPrefillTileRows);
+  return full >= kPrefillFillWorkgroups ? kPrefillTileRows : kPrefillTileRows / 2;
+}
 hipError_t launch_chunk_attn(const ChunkAttnArgs& a, hipStream_t stream);
 hipError_t launch_prefill_attn(const ChunkAttnArgs& a, hipStream_t stream);
 

@@ -20,6 +20,8 @@ pytestmark = pytest.mark.gpu
 # ---- the named prefill workloads -------------------------------------------------------------
 
 def test_prefill_pool_8k_splits_and_determinism():
+    """Splits 1 and 3 leave 256-row tiles short of the chip, so they run 128-row tiles (two waves
+    per row group, one per half of each chunk's keys); 0 (auto, 4) and 7 run 256-row tiles."""
     c, _ = workload("prefill_pool_8k")
     say("prefill_pool_8k: oracle")
     ref = run_oracle(c)
