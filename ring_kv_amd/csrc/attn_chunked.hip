@@ -5,22 +5,24 @@
 // ring_size/64 chunk slots in which logical chunk c sits in slot c mod (ring_size/64), so
 // both stores go through one kernel that differs only in the chunk -> slot rule.
 //
-// One workgroup = one KV head g and one range of whole chunks (a split).  Its rows are the
-// q_len * G (query, query-head) pairs that read head g; wave w owns rows 16w .. 16w+15.
-// Per chunk, for every wave:
-//   S^T [64 keys x 16 rows] = K [64 x D] . Q^T       4 x (D/32) MFMA 16x16x32 bf16
-//   online softmax over the chunk's 64 keys per row   (f32, exp2 domain)
-//   O^T [D x 16 rows]     += V^T [D x 64] . P^T       (D/16) x 2 MFMA
-// Computing S transposed leaves each lane with 16 scores of ONE row, which is exactly the
+// One workgroup = one KV head g, one range of whole chunks (a split) and one tile of 64 of the
+// q_len * G (query, query-head) rows that read head g.  Its 8 waves are 4 row groups x 2 key
+// halves: wave (rg, kh) owns rows 16rg .. 16rg+15 of the tile and keys 32kh .. 32kh+31 of every
+// chunk, keeps its own online-softmax state, and the two halves of a row group merge their
+// states through LDS at the end.  Per chunk, for every wave:
+//   S^T [32 keys x 16 rows] = K [32 x D] . Q^T       2 x (D/32) MFMA 16x16x32 bf16
+//   online softmax over its 32 keys per row           (f32, exp2 domain)
+//   O^T [D x 16 rows]     += V^T [D x 32] . P^T       D/16 MFMA, plus one for the row sum
+// Computing S transposed leaves each lane with scores of ONE row, which is exactly the
 // B-operand layout of P^T for the second product: no LDS round trip for P.  Within a pair
 // of 16-key tiles the key order is permuted (sigma below) so that each lane's 8 P values
 // are 8 consecutive keys, which the dimension-major V chunk supplies as one 16-byte read.
 //
 // Memory path: K and V chunks stream from HBM with 16-byte loads (a wave reads 1 KiB contiguous
-// per instruction) three chunks ahead of the compute, staged in registers and written into a
-// three-buffer ring of XOR-swizzled LDS tiles that all waves read.  (The direct HBM-to-LDS loads
-// of gfx950 were measured here at ~6 TB/s against ~7 TB/s for register loads of the same
-// blocks, so the data takes the register path.)
+// per instruction) two chunks ahead of the compute, staged in registers and written into two
+// XOR-swizzled LDS tiles that all waves read.  (The direct HBM-to-LDS loads of gfx950 were
+// measured here at ~6 TB/s against ~7 TB/s for register loads of the same blocks, so the data
+// takes the register path.)
 #include "rkv_device.hpp"
 #include "rkv_launch.hpp"
 
