@@ -71,6 +71,42 @@ def test_prefill_pool_131k_sampled_rows():
         assert_attn_close((out[i:i + 1], lse[i:i + 1]), want, "bf16", f"131k row {i}")
 
 
+
+@pytest.mark.parametrize("store,q_len,hq,hkv,d", [("paged", 4096, 16, 4, 128),
+                                                  ("ring", 4096, 16, 4, 128),
+                                                  ("paged", 16384, 2, 2, 64)])
+def test_prefill_max_rows_sampled(store, q_len, hq, hkv, d):
+    """The largest block one call may carry, RKV_MAX_ROWS = 16,384 rows per KV head (4,096
+    queries x 4 query heads per KV head: 256-row tiles; or 16,384 queries without grouping on 2
+    KV heads: 128-row tiles), over the pool and over a ring that holds every query's window.
+    Every row is computed; sampled rows (both ends, tile and chunk edges) are checked against the
+    oracle as single-token decodes at their own positions."""
+    if store == "paged":
+        c = paged_case(926, q_len, q_len + 904, q_len, hq, hkv, d, keep_rows=False)
+        p0 = c.ctx_len - q_len
+    else:
+        R, W = 4608, 512                      # R = W + q_len: the smallest multiple of 64 that holds
+        c = ring_case(927, q_len, 70000, q_len, hq, hkv, d, R, W)
+        p0 = c.pos0
+    assert q_len * (hq // hkv) == 16384
+    rows = (0, 1, 31, 32, 63, 64, 127, 128, 2047, 2048, q_len - 65, q_len - 2, q_len - 1)
+    want = {}
+    for i in rows:
+        if store == "paged":
+            want[i] = oracle.attention_paged(c.q[i:i + 1], c.k_pool, c.v_pool, c.page_table,
+                                             p0 + i + 1)
+        else:
+            want[i] = oracle.attention_ring(c.q[i:i + 1], c.k_ring, c.v_ring, p0 + i,
+                                            (p0 + i) % c.ring_size, c.ring_size, c.window)
+    # auto splits, and one split (which leaves the G = 1 block on 128-row tiles)
+    for splits in (0, 1):
+        say(f"prefill max rows {store} q_len={q_len} hq={hq} hkv={hkv} d={d} splits={splits}")
+        out, lse = run_gpu(c, num_splits=splits)
+        assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+        for i in rows:
+            assert_attn_close((out[i:i + 1], lse[i:i + 1]), want[i], "bf16",
+                              f"max rows {store} splits={splits} row {i}")
+
 # ---- exact coverage: zero Q, one-hot V -> each row's output counts its visible keys -------------
 
 def _one_hot_v(n, first, hkv, d):
