@@ -262,7 +262,7 @@ def config_timings(torch, rk, synth, probe, n_small, n_large):
     q, k, v = t(c.q), t(c.k_rows), t(c.v_rows)
     o1, l1 = f32(16, 8, 64), f32(16, 8)
     entry("contig_1k_f32", [lambda: rk.decode_attn_ref_layout(q, k, v, 1024, out=o1, lse=l1)],
-          n_small, c.kv_bytes, attn_flops(c), 157.3, "fp32_vector",
+          n_small, c.kv_bytes, attn_flops(c), 157.3, "mfma_fp32",
           "decode_attn_ref_layout, auto splits; bound: launch latency")
     lg, pr = t(acc.logits), t(acc.proposals)
     al, cm, am = (torch.empty(n, dtype=torch.int32, device="cuda") for n in (1, 17, 17))
