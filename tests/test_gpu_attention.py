@@ -219,6 +219,33 @@ def test_determinism_and_two_phase():
                 assert abs(pln[g, s, r] - l[i, h]) <= 2e-3
 
 
+@pytest.mark.parametrize("kind,ctx_or_pos,q_len,window", [("paged", 1, 1, 0), ("contig", 1, 1, 0),
+                                                         ("ring", 0, 1, 512), ("ring", 30000, 16, 1),
+                                                         ("contig", 1024, 16, 1)])
+def test_degenerate_contexts(kind, ctx_or_pos, q_len, window):
+    """A context of one key, and a window of one key (each query sees only its own row): the
+    softmax has a single term, so every output row is that key's V and the lse is its scaled
+    score; checked against the oracle and against the V rows themselves."""
+    hq, hkv, d = 16, 4, 128
+    if kind == "paged":
+        c = paged_case(940, 0, ctx_or_pos, q_len, hq, hkv, d)
+    elif kind == "contig":
+        c = contig_case(941, ctx_or_pos, ctx_or_pos, q_len, hq, hkv, 64, "f32", window=window)
+        d = 64
+    else:
+        c = ring_case(942, ctx_or_pos, ctx_or_pos, q_len, hq, hkv, d, 2048, window)
+    say(f"degenerate {kind} ctx/pos={ctx_or_pos} q_len={q_len} window={window}")
+    out, lse = run_gpu(c)
+    assert_attn_close((out, lse), run_oracle(c), c.dtype, f"degenerate {kind}")
+    G = hq // hkv
+    first_q = c.ctx_len - q_len
+    v = oracle.to_f64(c.v_rows, c.dtype)
+    for i in range(q_len):
+        p = first_q + i
+        for h in range(hq):
+            np.testing.assert_allclose(out[i, h], v[p - c.rows_first, h // G], rtol=1e-6, atol=1e-7)
+
+
 def test_verify_row_equals_single_token_decode():
     c, _ = workload("paged_8k")
     say("verify vs decode (q_len=1)")
