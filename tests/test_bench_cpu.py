@@ -1,0 +1,60 @@
+"""Host logic of bench.py (CPU): the one-GPU guard and the HBM-traffic arithmetic that turns
+rocprofv3 FETCH_SIZE / WRITE_SIZE counters into bytes per launch."""
+import csv
+import json
+import os
+import subprocess
+import sys
+from types import SimpleNamespace
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def _counters(path, rows):
+    """A counter_collection.csv with one row per (kernel name, KiB per dispatch)."""
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for i, (name, kib) in enumerate(rows):
+            w.writerow([i + 1, name, "X", kib])
+    return str(path)
+
+
+def test_traffic_is_scaled_by_the_plain_copy(tmp_path, monkeypatch):
+    """A 1 GiB copy whose FETCH_SIZE reads half its bytes and whose WRITE_SIZE reads them all
+    gives scales 2 and 1; the kernel's mean counter per dispatch is scaled by them."""
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    kern = "void rkv::(anonymous namespace)::chunk_attn_kernel<128, 4, 2, true>(rkv::ChunkAttnArgs)"
+    other = "void at::native::vectorized_elementwise_kernel<4>(int)"
+    args = SimpleNamespace(
+        copy_fetch=_counters(tmp_path / "cf.csv", [("__amd_rocclr_copyBuffer", 524288.0)]),
+        copy_write=_counters(tmp_path / "cw.csv", [("__amd_rocclr_copyBuffer", 1048576.0)]),
+        fetch=_counters(tmp_path / "kf.csv", [(kern, 131000.0), (other, 9e9), (kern, 131144.0)]),
+        write=_counters(tmp_path / "kw.csv", [(kern, 8256.0), (kern, 8256.0)]))
+    bench.traffic_summary(args)
+    t = json.load(open(tmp_path / "traffic.json"))
+    assert t["dispatches"] == 2
+    assert t["fetch_scale"] == 2.0 and t["write_scale"] == 1.0
+    assert t["hbm_fetch_bytes_per_launch"] == 131072 * 1024 * 2       # mean of the two dispatches
+    assert t["hbm_write_bytes_per_launch"] == 8256 * 1024
+    assert t["algorithmic_bytes_per_launch"] == 2 * 131072 * 4 * 128 * 2
+    assert t["traffic_over_algorithmic"] == round((268435456 + 8454144) / 268435456, 4)
+    assert t["kernel_sha"] == bench.kernel_hash()
+
+
+def test_traffic_is_dropped_once_the_kernel_source_changes(tmp_path, monkeypatch):
+    f = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    f.write_text(json.dumps({"kernel_sha": bench.kernel_hash(), "hbm_bytes_per_launch": 123}))
+    assert bench.traffic_entry(268435456) == 123
+    f.write_text(json.dumps({"kernel_sha": "0" * 16, "hbm_bytes_per_launch": 123}))
+    assert bench.traffic_entry(268435456) is None
