@@ -81,29 +81,56 @@ __global__ __launch_bounds__(256) void accept_partial_kernel(AcceptArgs a) {
   }
 }
 
+// Pass 2 reduces each row's parts with a group of GP lanes (the part count rounded up to a power
+// of two, at most 64), 256 / GP rows side by side; every thread issues its loads for kRounds such
+// rounds before its first compare, so the step's 17 rows of 16 parts cost one memory round trip.
+constexpr int kRounds = 4;
+
 __global__ __launch_bounds__(256) void accept_final_kernel(AcceptArgs a) {
   __shared__ int t[256];
   __shared__ int prop[256];
   __shared__ int acc_len;
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
   const int n_draft = a.n_rows - 1;
   if (tid < n_draft) prop[tid] = a.proposals[tid];
-  // wave w reduces rows w, w+4, ...: lane p takes parts p, p+64, ... (one load round for up
-  // to 64 parts), then a shuffle reduction
-  for (int row2 = w; row2 < a.n_rows; row2 += 4) {
-    float rv = -INFINITY;
-    int ri = INT_MAX;
-    for (int p = tid & 63; p < a.parts; p += 64) {
-      const float v = a.part_val[(int64_t)row2 * a.parts + p];
-      const int i = a.part_idx[(int64_t)row2 * a.parts + p];
-      if (better(v, i, rv, ri)) { rv = v; ri = i; }
+  int GP = 1;
+  while (GP < a.parts && GP < 64) GP <<= 1;
+  const int rpr = 256 / GP;                 // rows per round
+  const int lg = tid % GP;                  // this lane's place in its row's group
+  for (int r0 = 0; r0 < a.n_rows; r0 += rpr * kRounds) {
+    float lv[kRounds];
+    int li[kRounds];
+#pragma unroll
+    for (int k = 0; k < kRounds; ++k) {     // clamped, so every load is in range and issued
+      const int row = min(r0 + k * rpr + tid / GP, a.n_rows - 1);
+      const int64_t off = (int64_t)row * a.parts + min(lg, a.parts - 1);
+      lv[k] = a.part_val[off];
+      li[k] = a.part_idx[off];
     }
-    wave_argmax(rv, ri);
-    if ((tid & 63) == 0) {
-      if (ri == INT_MAX) ri = 0;   // a row of NaNs only: any in-range index
-      t[row2] = ri;
-      if (a.row_argmax != nullptr) a.row_argmax[row2] = ri;
+#pragma unroll
+    for (int k = 0; k < kRounds; ++k) {
+      const int row = r0 + k * rpr + tid / GP;
+      float bv = -INFINITY;
+      int bi = INT_MAX;
+      if (row < a.n_rows && lg < a.parts && better(lv[k], li[k], bv, bi)) { bv = lv[k]; bi = li[k]; }
+      // parts beyond the first 64 (vocabularies above 64 x 4,096)
+      if (row < a.n_rows) {
+        for (int p = lg + GP; p < a.parts; p += GP) {
+          const float v = a.part_val[(int64_t)row * a.parts + p];
+          const int i = a.part_idx[(int64_t)row * a.parts + p];
+          if (better(v, i, bv, bi)) { bv = v; bi = i; }
+        }
+      }
+      for (int off = GP >> 1; off >= 1; off >>= 1) {   // within the aligned group of GP lanes
+        const float ov = __shfl_xor(bv, off, kWave);
+        const int oi = __shfl_xor(bi, off, kWave);
+        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+      }
+      if (lg == 0 && row < a.n_rows) {
+        const int ri = bi == INT_MAX ? 0 : bi;   // a row of NaNs only: any in-range index
+        t[row] = ri;
+        if (a.row_argmax != nullptr) a.row_argmax[row] = ri;
+      }
     }
   }
   __syncthreads();
