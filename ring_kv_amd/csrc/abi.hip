@@ -49,6 +49,23 @@ int64_t auto_split_target(const rkv_attn_dims* d, Store store) {
   return (kTargetWorkgroups + units - 1) / units;
 }
 
+// The paged store's automatic split target for a context of n_chunks chunks.  A verify block's
+// merge reads one partial per split and row, so below about 256 chunks fewer, longer splits win:
+// at least n_chunks / 4 and half the fill target, never more than the chunks (one chunk per split
+// keeps its single-round-trip path) nor the fill target.  Measured in graph replay (16 query / 4
+// KV heads): 4,096 positions 13.2 -> 12.4 us, 8,192: 15.5 -> 14.3 us, 12,288: 17.0 -> 15.7 us;
+// from 16,384 positions on the fill target stays best.  Monotone in n_chunks.  Prefill blocks keep
+// the fill target.
+int64_t paged_split_target(const rkv_attn_dims* d, int64_t n_chunks) {
+  const int64_t t = auto_split_target(d, kPaged);
+  if (rows_of(d) > rkv::kVerifyMaxRows) return t;
+  const int64_t half = t / 2 > 1 ? t / 2 : 1;
+  const int64_t lo = n_chunks < half ? n_chunks : half;
+  const int64_t quarter = (n_chunks + 3) / 4;
+  const int64_t want = lo > quarter ? lo : quarter;
+  return want < t ? want : t;
+}
+
 // Split n_chunks whole chunks into ranges: num_splits <= 0 asks for `target` splits.  Returns
 // the split count actually used (no empty split unless the caller asked for more splits than
 // chunks) and the chunks per split.
@@ -313,7 +330,8 @@ int32_t verify_attn_paged_auto_splits(const rkv_attn_dims* dims, int64_t ctx_len
                                       int32_t chunk_size) {
   if (check_dims(dims) != RKV_OK || chunk_size != kChunk || ctx_len < 1) return 0;
   int32_t s, cps;
-  choose_splits((ctx_len + kChunk - 1) / kChunk, auto_split_target(dims, kPaged), 0, &s, &cps);
+  const int64_t n = (ctx_len + kChunk - 1) / kChunk;
+  choose_splits(n, paged_split_target(dims, n), 0, &s, &cps);
   return s;
 }
 
@@ -323,8 +341,8 @@ size_t verify_attn_paged_workspace_bytes(const rkv_attn_dims* dims, int64_t ctx_
       num_splits < 0)
     return 0;
   int32_t s, cps;
-  choose_splits((ctx_len + kChunk - 1) / kChunk, auto_split_target(dims, kPaged), num_splits,
-                &s, &cps);
+  const int64_t n = (ctx_len + kChunk - 1) / kChunk;
+  choose_splits(n, paged_split_target(dims, n), num_splits, &s, &cps);
   return partial_bytes(dims, s);
 }
 
@@ -339,7 +357,7 @@ int32_t verify_attn_paged(const rkv_attn_dims* dims, const void* q, const void* 
   if (out == nullptr) return RKV_ERR_NULL;
   if (num_splits < 0) return RKV_ERR_ARG;
   ChunkAttnArgs a = paged_args(dims, q, k_pool, v_pool, page_table, n_slots, ctx_len);
-  choose_splits(a.n_chunks, auto_split_target(dims, kPaged), num_splits, &a.num_splits,
+  choose_splits(a.n_chunks, paged_split_target(dims, a.n_chunks), num_splits, &a.num_splits,
                 &a.cps);
   if (a.num_splits > 1 &&
       (workspace == nullptr || workspace_bytes < partial_bytes(dims, a.num_splits)))

@@ -71,9 +71,16 @@ def test_paged_workspace_and_splits():
     want = 4 * 64 * 64 * 128 * 4 + 4 * 64 * 64 * 4
     assert L.verify_attn_paged_workspace_bytes(d, 262144, 64, 0) == want
     assert L.verify_attn_paged_workspace_bytes(d, 262144, 64, 1) == 0     # no merge, no partials
-    assert L.verify_attn_paged_auto_splits(d, 8192, 64) == 64            # 2 chunks per split
     assert L.verify_attn_paged_auto_splits(d, 131072, 64) == 64
+    # shorter contexts: fewer, longer splits (a smaller merge), at least n/4 and 32, at most n
+    assert L.verify_attn_paged_auto_splits(d, 16384, 64) == 64           # 4 chunks per split
+    assert L.verify_attn_paged_auto_splits(d, 12288, 64) == 48
+    assert L.verify_attn_paged_auto_splits(d, 8192, 64) == 32            # 4 chunks per split
+    assert L.verify_attn_paged_auto_splits(d, 4096, 64) == 32            # 2 chunks per split
+    assert L.verify_attn_paged_auto_splits(d, 1024, 64) == 16            # 1 chunk per split
     assert L.verify_attn_paged_auto_splits(d, 65, 64) == 2
+    want8k = 4 * 32 * 64 * 128 * 4 + 4 * 32 * 64 * 4
+    assert L.verify_attn_paged_workspace_bytes(d, 8192, 64, 0) == want8k
     assert L.verify_attn_paged_workspace_bytes(d, 262144, 32, 0) == 0    # unsupported chunk
 
 
@@ -217,12 +224,14 @@ def test_resident_attention_checks():
 
 
 def test_resident_workspace_is_that_of_its_chunks():
-    # the resident call splits the n_res listed chunks like a context of 64 * n_res positions:
-    # 47 chunks take 47 splits of one chunk, more than the 41 of the full 81-chunk context
+    # the resident call splits the n_res listed chunks like a context of 64 * n_res positions,
+    # and split counts are not monotone in the context: 32 chunks take 32 splits of one chunk,
+    # more than the 20 of the full 40-chunk context
     d = dims()
-    assert L.verify_attn_paged_auto_splits(d, 64 * 47, 64) == 47
-    assert L.verify_attn_paged_auto_splits(d, 5136, 64) == 41
-    short = L.verify_attn_paged_workspace_bytes(d, 5136, 64, 0)
-    assert short < L.verify_attn_paged_workspace_bytes(d, 64 * 48, 64, 0)
-    assert L.verify_attn_paged_resident(d, P, P, P, P, _i32(*range(33, 81)), 48, 160, 5136, 0,
+    assert L.verify_attn_paged_auto_splits(d, 64 * 32, 64) == 32
+    assert L.verify_attn_paged_auto_splits(d, 2560, 64) == 20
+    short = L.verify_attn_paged_workspace_bytes(d, 2560, 64, 0)
+    assert short < L.verify_attn_paged_workspace_bytes(d, 64 * 32, 64, 0)
+    # chunks 8..38 resident plus the block's chunk 39: a packed context of 32 chunks
+    assert L.verify_attn_paged_resident(d, P, P, P, P, _i32(*range(8, 40)), 32, 160, 2560, 0,
                                         P, short, P, NULL, NULL) == EWS
