@@ -128,7 +128,9 @@ int32_t decode_attn_ref_layout(const rkv_attn_dims* dims, const void* q, const v
  * [ring_size/64][Hkv][D][64], bf16; Q bf16.  Slots holding no position may contain
  * anything (they are masked and never multiply a result).
  * The span of the window is split into num_splits ranges of whole chunks (0: one chunk
- * per range, every chunk in flight at once) whose partials a log-sum-exp merge combines.
+ * per range, every chunk in flight at once, for a verify block; a block of more than 256
+ * rows per KV head is not split, its row tiles fill the chip) whose partials a
+ * log-sum-exp merge combines.
  * One range spans at most 2^22 chunks (RKV_ERR_SHAPE otherwise).
  * ------------------------------------------------------------------------------- */
 size_t verify_attn_ring_workspace_bytes(const rkv_attn_dims* dims, int32_t ring_size,
