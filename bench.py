@@ -578,35 +578,56 @@ CPU_SAMPLE_MIN_SECONDS = 10.0
 def cpu_baseline(synth, oracle):
     """The fp64 oracle on a bounded sample of the step, timed on the host cores: one paged layer
     at 131,072, three ring layers and the accept (the step's 1:3 mix of layer types; ten samples
-    are one step's work), repeated until at least CPU_SAMPLE_MIN_SECONDS of work."""
+    are one step's work), repeated until at least CPU_SAMPLE_MIN_SECONDS of work.  Returns the
+    oracle's results of the sample (by layer, and "accept") and the baseline entry."""
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
         threads = len(os.sched_getaffinity(0))
-    cases = [synth.workload("stack_40l_131k", l, keep_rows=False)[0] for l in (3, 0, 1, 2)]
+    layer_ids = (3, 0, 1, 2)
+    cases = [synth.workload("stack_40l_131k", l, keep_rows=False)[0] for l in layer_ids]
     acc = synth.workload("stack_40l_131k", 0, keep_rows=False)[1]
     kv = sum(c.kv_bytes for c in cases)
     reps, dt = 0, 0.0
+    results = {}
     while dt < CPU_SAMPLE_MIN_SECONDS:
         t0 = time.perf_counter()
-        for c in cases:
+        for l, c in zip(layer_ids, cases):
             if c.kind == "paged":
-                oracle.attention_paged(c.q, c.k_pool, c.v_pool, c.page_table, c.ctx_len)
+                r = oracle.attention_paged(c.q, c.k_pool, c.v_pool, c.page_table, c.ctx_len)
             else:
-                oracle.attention_ring(c.q, c.k_ring, c.v_ring, c.pos0, c.ring_head, c.ring_size,
-                                      c.window)
-        oracle.greedy_accept(acc.logits, acc.proposals)
+                r = oracle.attention_ring(c.q, c.k_ring, c.v_ring, c.pos0, c.ring_head,
+                                          c.ring_size, c.window)
+            results.setdefault(l, r)
+        results.setdefault("accept", oracle.greedy_accept(acc.logits, acc.proposals))
         dt += time.perf_counter() - t0
         reps += 1
     model, blas = cpu_info()
-    return {"value": round(kv * reps / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+    return results, {"value": round(kv * reps / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle", "seconds": round(dt, 3), "samples": reps,
             "sample": f"1 paged layer (ctx 131,072) + 3 ring layers + accept [17x65536] of the "
                       f"40-layer step (its 1:3 mix of layer types), {reps} times in a row (10 "
                       f"times = one step's work); KV bytes of the samples / wall time",
             "cpu": model, "blas": blas,
             "us_per_call": oracle_per_config(synth, oracle)}
+
+
+def step_parity(step_out, ref):
+    """The timed step's own outputs of layers 0-3 (three window layers, one paged layer at
+    131,072) and of the accept, against the fp64 oracle's results of the baseline sample."""
+    import numpy as np
+    layers = sorted(k for k in ref if k != "accept")
+    err_o = max(float(np.abs(step_out[l][0] - ref[l][0]).max()) for l in layers)
+    err_l = max(float(np.abs(step_out[l][1] - ref[l][1]).max()) for l in layers)
+    a, committed = step_out["accept"]
+    ra, rcommitted, _ = ref["accept"]
+    exact = a == ra and np.array_equal(committed[:a + 1], rcommitted) and \
+        bool(np.all(committed[a + 1:] == -1))
+    return {"layers": layers, "max_abs_out": err_o, "max_abs_lse": err_l, "tolerance": 1e-2,
+            "within_tolerance": err_o <= 1e-2 and err_l <= 1e-2, "accept_exact": exact,
+            "note": "the timed step's outputs of these layers and of the accept [17 x 65,536] "
+                    "against the fp64 oracle (the cpu_baseline sample)"}
 
 
 def counter_kib(path, kernel_substr):
@@ -801,6 +822,9 @@ def main():
                          "algorithmic_bytes_per_launch": per_launch,
                          "traffic": traffic_entry(per_launch)},
         })
+        step_out = {l: (st.layers[l]["out"].cpu().numpy(), st.layers[l]["lse"].cpu().numpy())
+                    for l in (0, 1, 2, 3)}
+        step_out["accept"] = (int(st.acc_len.cpu()[0]), st.committed.cpu().numpy())
         del st
         torch.cuda.empty_cache()
 
@@ -894,7 +918,9 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         log("cpu baseline (oracle)")
-        res["cpu_baseline"] = cpu_baseline(synth, oracle)
+        ref, res["cpu_baseline"] = cpu_baseline(synth, oracle)
+        if args.workload == "stack_40l_131k":
+            res["parity"] = step_parity(step_out, ref)
     print(json.dumps(res), flush=True)
 
 

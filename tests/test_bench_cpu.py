@@ -58,3 +58,22 @@ def test_traffic_is_dropped_once_the_kernel_source_changes(tmp_path, monkeypatch
     assert bench.traffic_entry(268435456) == 123
     f.write_text(json.dumps({"kernel_sha": "0" * 16, "hbm_bytes_per_launch": 123}))
     assert bench.traffic_entry(268435456) is None
+
+
+def test_step_parity_compares_outputs_and_the_accept():
+    import numpy as np
+    g = np.random.default_rng(5)
+    ref = {l: (g.standard_normal((16, 16, 128)), g.standard_normal((16, 16))) for l in (3, 0, 1, 2)}
+    ref["accept"] = (2, np.array([7, 9, 4], np.int32), np.zeros(17, np.int32))
+    committed = np.array([7, 9, 4] + [-1] * 14, np.int32)
+    same = {l: (ref[l][0].astype(np.float32), ref[l][1].astype(np.float32)) for l in (0, 1, 2, 3)}
+    same["accept"] = (2, committed)
+    p = bench.step_parity(same, ref)
+    assert p["layers"] == [0, 1, 2, 3] and p["within_tolerance"] and p["accept_exact"]
+    assert p["max_abs_out"] < 1e-6 and p["max_abs_lse"] < 1e-6
+    off = dict(same)
+    off[3] = (same[3][0] + 0.02, same[3][1])
+    off["accept"] = (2, np.array([7, 9, 5] + [-1] * 14, np.int32))
+    p = bench.step_parity(off, ref)
+    assert not p["within_tolerance"] and not p["accept_exact"]
+    assert abs(p["max_abs_out"] - 0.02) < 1e-5
