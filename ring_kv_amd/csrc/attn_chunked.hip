@@ -61,6 +61,14 @@ __device__ __forceinline__ float row_max4(float v) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// sum over the four lanes of a row, the same value (and the same bits) on all four
+__device__ __forceinline__ float row_sum4(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Positions inside a workgroup are 32-bit offsets from its split's first key, clamped to
 // +-2^29 (a split spans at most kMaxSplitChunks chunks, 2^28 positions), so every edge test is a
 // 32-bit scalar or vector compare.
@@ -252,8 +260,12 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
   // ---- running softmax state ---------------------------------------------------------
   // m_run: exp2-domain reference max of this lane's row over the wave's keys.  oacc holds
   // sum_j p_j V_j^T and lacc the row sum sum_j p_j (computed by the matrix core against a
-  // column of ones, so it uses exactly the bf16 weights the PV product uses).
+  // column of ones, so it uses exactly the bf16 weights the PV product uses: the output's
+  // normaliser).  lf is this lane's share of the same sum over the f32 weights, for the lse:
+  // a row dominated by one key would otherwise carry that weight's bf16 rounding (up to 2^-8)
+  // into its lse.
   float m_run = -INFINITY;
+  float lf = 0.f;
   f32x4 oacc[TMD];
   f32x4 lacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -314,6 +326,7 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
 #pragma unroll
       for (int t = 0; t < TMD; ++t) oacc[t] *= alpha;
       lacc *= alpha;
+      lf *= alpha;
       m_run = m_new;
     }
     // a row with no visible key yet keeps m_run = -inf; its weights must come out 0, not NaN
@@ -330,6 +343,7 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
         const float p3 = __builtin_amdgcn_exp2f(fmaf(sacc[j][3], csc, -m_use));
         pw[h][2 * hh] = pack_bf16x2(p0, p1);
         pw[h][2 * hh + 1] = pack_bf16x2(p2, p3);
+        lf += (p0 + p1) + (p2 + p3);
       }
     }
 #pragma unroll
@@ -516,11 +530,14 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
   // ---- epilogue ------------------------------------------------------------------------
   // row sum: component 0 of lacc in lane ln (lane group 0); every lane of the row needs it
   float l = __shfl(lacc[0], ln, kWave);
+  float lfr = row_sum4(lf);
   if constexpr (KS == 2) {
-    // key half 1 hands (m, l, O) to key half 0 through LDS; every chunk load has landed
+    // key half 1 hands (m, l, lf, O) to key half 0 through LDS; every chunk load has landed
     float* xo = reinterpret_cast<float*>(&lds[0][0]);          // [NRG][16][D]
     float* xm = xo + NRG * 16 * D;                               // [NRG][16]
     float* xl = xm + NRG * 16;
+    float* xf = xl + NRG * 16;
+    static_assert((NRG * 16 * D + 3 * NRG * 16) * 4 <= NLDS * T::elems * 2, "exchange fits");
     // row (rg, ln), 16-byte column 4t + lq of D/4, XOR-swizzled by the row so that the 16
     // lanes of one access group (16 rows, same column) land in 16 different bank groups
     auto xo_off = [&](int t) __attribute__((always_inline)) {
@@ -534,6 +551,7 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
       if (lq == 0) {
         xm[rg * 16 + ln] = m_run;
         xl[rg * 16 + ln] = l;
+        xf[rg * 16 + ln] = lfr;
       }
     }
     lds_barrier();
@@ -546,6 +564,7 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
       const float a0 = __builtin_amdgcn_exp2f(m_run - Mu);
       const float a1 = __builtin_amdgcn_exp2f(m1 - Mu);
       l = a0 * l + a1 * l1;
+      lfr = a0 * lfr + a1 * xf[rg * 16 + ln];
 #pragma unroll
       for (int t = 0; t < TMD; ++t) {
         const f32x4 o1 = *reinterpret_cast<const f32x4*>(&xo[xo_off(t)]);
@@ -556,7 +575,7 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
   }
   if (!wave_active || !row_ok) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  const float lse_nat = l > 0.f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+  const float lse_nat = lfr > 0.f ? (m_run + log2f(lfr)) * kLn2 : -INFINITY;
   float* dst;
   if (a.part_o == nullptr) {
     dst = a.out + ((int64_t)qi * a.n_q_heads + hq) * D;

@@ -246,6 +246,24 @@ def test_degenerate_contexts(kind, ctx_or_pos, q_len, window):
             np.testing.assert_allclose(out[i, h], v[p - c.rows_first, h // G], rtol=1e-6, atol=1e-7)
 
 
+@pytest.mark.parametrize("scale", [0.01, 1.0, 4.0])
+@pytest.mark.parametrize("kind,q_len", [("paged", 16), ("paged", 700), ("ring", 16), ("ring", 600)])
+def test_custom_scale(kind, q_len, scale):
+    """A softmax scale other than 1/sqrt(D): near-uniform weights (0.01) and scores spread over
+    hundreds in the exp2 domain (4.0, about 45 standard deviations), where the running maxima are
+    replaced often; verify blocks and prefill-sized blocks, pool and ring, against the oracle."""
+    if kind == "paged":
+        c = paged_case(950, q_len, 3000 + q_len, q_len, 16, 4, 128)
+        want = oracle.attention_paged(c.q, c.k_pool, c.v_pool, c.page_table, c.ctx_len,
+                                      scale=scale)
+    else:
+        c = ring_case(951, q_len, 30000, q_len, 16, 4, 128, 2048, 512)
+        want = oracle.attention_ring(c.q, c.k_ring, c.v_ring, c.pos0, c.ring_head, c.ring_size,
+                                     c.window, scale=scale)
+    say(f"custom scale {scale} {kind} q_len={q_len}")
+    assert_attn_close(run_gpu(c, scale=scale), want, "bf16", f"scale {scale} {kind} {q_len}")
+
+
 def test_verify_row_equals_single_token_decode():
     c, _ = workload("paged_8k")
     say("verify vs decode (q_len=1)")
