@@ -1,4 +1,5 @@
-"""A verify step (ring layers, a paged layer, the accept) captured in a HIP graph and replayed:
+"""Entry points captured in HIP graphs and replayed (a verify step; prefill blocks, the resident
+call and host paging):
 every replay must reproduce the eager results bit for bit, with eager work and
 synchronisations between the replays; and one accept workspace serves many calls in a row."""
 import numpy as np
@@ -78,3 +79,85 @@ def test_graph_replay_matches_eager():
         say(f"graph: replay {rep}")
         for a, b in zip(got, ref):
             assert torch.equal(a, b), f"replay {rep} differs from the eager step"
+
+
+def test_graph_replay_prefill_resident_and_paging():
+    """The other entry points in a HIP graph: a 1,024-token prefill block over the pool (matrix-
+    core kernel, 4 splits, row-parallel merge) and over the ring (128-row tiles), attention over a
+    resident subset, and a page-out to pinned host memory followed by a page-in of long runs
+    (copy engines) and of scattered ids (direct kernel).  Every replay reproduces the eager
+    results bit for bit, with the outputs, the host store and the target pool clobbered by eager
+    work between replays."""
+    import ctypes
+    from ring_kv_amd._lib import AttnDims
+    L = rk.lib()
+    pf = paged_case(32, 0, 9216, 1024, 16, 4, 128, keep_rows=False)
+    rf = ring_case(33, 0, 30000, 1024, 16, 4, 128, 2048, 512, keep_rows=False)
+    vr = paged_case(34, 0, 4096, 16, 16, 4, 128, keep_rows=False)
+    Pq, Pk, Pv, Pt = dev(pf.q), dev(pf.k_pool), dev(pf.v_pool), dev(pf.page_table)
+    Rq, Rk, Rv = dev(rf.q), dev(rf.k_ring), dev(rf.v_ring)
+    Vq, Vk, Vv = dev(vr.q), dev(vr.k_pool), dev(vr.v_pool)
+    keep = [0, 3, 5, 9, 10, 11, 20, 31, 40] + list(range(60, 64))
+    vslots = dev(np.array([int(vr.page_table[c]) for c in keep], np.int32))
+    d16, d1024 = AttnDims(16, 16, 4, 128, 0.0, 1), AttnDims(1024, 16, 4, 128, 0.0, 1)
+    ws_pf = torch.empty(L.verify_attn_paged_workspace_bytes(ctypes.byref(d1024), 9216, 64, 0),
+                        dtype=torch.uint8, device="cuda")
+    ws_res = torch.empty(max(1, L.verify_attn_paged_workspace_bytes(
+        ctypes.byref(d16), 64 * len(keep), 64, 0)), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty(q, 16, 128, device="cuda") for q in (1024, 1024, 16)]
+    lses = [torch.empty(q, 16, device="cuda") for q in (1024, 1024, 16)]
+    # paging: 40 pool slots out to 96 host entries, then back into another pool
+    hkv, d = 4, 128
+    src_k = Vk[:40].clone()
+    src_v = Vv[:40].clone()
+    kh = torch.zeros((96, hkv, 64, d), dtype=torch.bfloat16, pin_memory=True)
+    vh = torch.zeros((96, hkv, d, 64), dtype=torch.bfloat16, pin_memory=True)
+    out_slots = list(range(40))
+    out_ids = list(range(10, 30)) + [int(x) for x in np.random.default_rng(35).choice(
+        np.arange(40, 96), 20, replace=False)]
+    dst_k = torch.zeros_like(src_k)
+    dst_v = torch.zeros_like(src_v)
+    run_ids, run_slots = list(range(10, 30)), list(range(20))            # one long run
+    sc_ids, sc_slots = out_ids[20:], list(range(20, 40))                  # scattered
+    ws_pg = torch.empty(L.kv_page_workspace_bytes(hkv, d, 40), dtype=torch.uint8, device="cuda")
+
+    def work():
+        rk.verify_attn_paged(Pq, Pk, Pv, Pt, 9216, out=outs[0], lse=lses[0], workspace=ws_pf)
+        rk.verify_attn_ring(Rq, Rk, Rv, rf.pos0, 512, out=outs[1], lse=lses[1])
+        rk.verify_attn_paged_resident(Vq, Vk, Vv, vslots, keep, 4096, out=outs[2], lse=lses[2],
+                                      workspace=ws_res)
+        rk.kv_page_out(src_k, src_v, out_slots, out_ids, kh, vh, workspace=ws_pg)
+        rk.kv_page_in(kh, vh, run_ids, run_slots, dst_k, dst_v, workspace=ws_pg)
+        rk.kv_page_in(kh, vh, sc_ids, sc_slots, dst_k, dst_v, workspace=ws_pg)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return [t.clone() for t in (*outs, *lses, dst_k, dst_v)] + [kh.clone(), vh.clone()]
+
+    say("graph 2: eager reference")
+    work()
+    ref = snapshot()
+    assert torch.equal(ref[6], src_k) and torch.equal(ref[7], src_v)     # the round trip itself
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        work()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    say("graph 2: capture")
+    with torch.cuda.graph(g):
+        work()
+    for rep in range(4):
+        for t in (*outs, *lses):
+            t.fill_(-7)                                  # eager work between replays
+        dst_k.zero_()
+        dst_v.zero_()
+        torch.cuda.synchronize()
+        kh.zero_()
+        vh.zero_()
+        g.replay()
+        got = snapshot()
+        say(f"graph 2: replay {rep}")
+        for i, (a, b) in enumerate(zip(got, ref)):
+            assert torch.equal(a, b), f"replay {rep}: tensor {i} differs from the eager run"
