@@ -339,3 +339,24 @@ def test_p9_merge_skips_empty_parts():
     o, l = oracle.lse_merge([p1, p2])
     np.testing.assert_allclose(o[0, 0], [0.5, 0.5], atol=1e-15)
     assert abs(l[0, 0] - math.log(2)) < 1e-15
+
+
+def test_p9_merge_at_logits_beyond_exp_range():
+    """Scores in the thousands (lse 900 .. 2,500, where exp overflows float64): the merge still
+    equals the unsplit softmax, and every part carries a real share of the weight."""
+    hkv, hq, d, q_len, ctx = 2, 8, 16, 16, 700
+    g = np.random.default_rng(31)
+    k, v = g.standard_normal((ctx, hkv, d)), g.standard_normal((ctx, hkv, d))
+    q = g.standard_normal((q_len, hq, d)) * 500
+    whole = oracle.attention_contiguous(q, k, v, ctx, dtype="f64")
+    assert whole[1].min() > 710                 # exp(lse) is not representable
+    q_pos = np.arange(ctx - q_len, ctx)
+    bounds = [0, 100, 333, 650, ctx]
+    parts = [oracle.attention_partial(q, lambda gg, a=a, b=b: k[a:b, gg],
+                                      lambda gg, a=a, b=b: v[a:b, gg], np.arange(a, b), q_pos,
+                                      0, 1 / math.sqrt(d), hkv)
+             for a, b in zip(bounds[:-1], bounds[1:])]
+    assert all(np.exp(p[1] - whole[1]).mean() > 0.05 for p in parts)
+    o, l = oracle.lse_merge(parts)
+    np.testing.assert_allclose(o, whole[0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l, whole[1], rtol=1e-14, atol=0)

@@ -230,3 +230,97 @@ def test_evicting_the_partial_tail_chunk_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "PagerModel", Pager)
     with pytest.raises((AssertionError, pytest.fail.Exception)):   # "DID NOT RAISE"
         pin()
+
+
+# --- the merge and the accept: planted mistakes in copies of lse_merge / greedy_accept ---------
+
+def _merge_mutant(kind):
+    def lse_merge(parts):
+        lses = np.stack([np.asarray(l, dtype=np.float64) for _, l in parts])
+        outs = np.stack([np.asarray(o, dtype=np.float64) for o, _ in parts])
+        M = lses.max(axis=0)
+        has = np.isfinite(M)
+        Mz = np.where(has, M, 0.0) if kind != "no_max_shift" else np.zeros_like(M)
+        w = np.where(np.isfinite(lses), np.exp(lses - Mz[None]), 0.0)
+        if kind == "empty_part_weighted":
+            w = np.where(np.isfinite(lses), w, 1.0)
+        if kind == "equal_weights":
+            w = np.where(np.isfinite(lses), 1.0, 0.0)
+        tot = w.sum(axis=0)
+        num = (w[..., None] * outs).sum(axis=0)
+        out = np.zeros(outs.shape[1:], dtype=np.float64)
+        out[has] = num[has] if kind == "no_normalise" else num[has] / tot[has][..., None]
+        lse = np.full(M.shape, -np.inf)
+        lse[has] = M[has] if kind == "lse_is_max" else M[has] + np.log(tot[has])
+        return out, lse
+    return lse_merge
+
+
+def _merge_pins():
+    import test_oracle_attention as T
+    T.test_p9_split_merge_equals_unsplit(500)
+    T.test_p9_merge_skips_empty_parts()
+    T.test_p9_merge_at_logits_beyond_exp_range()
+
+
+@pytest.mark.parametrize("kind", ["no_max_shift", "empty_part_weighted", "equal_weights",
+                                  "no_normalise", "lse_is_max"])
+def test_merge_pins_catch_planted_mistakes(kind, monkeypatch):
+    _merge_pins()
+    monkeypatch.setattr(oracle, "lse_merge", _merge_mutant(kind))
+    with np.errstate(over="ignore", invalid="ignore"), pytest.raises(AssertionError):
+        _merge_pins()
+
+
+def _accept_mutant(kind):
+    def greedy_accept(logits, proposals, scan=False):
+        L = np.asarray(logits, dtype=np.float32)
+        prop = np.asarray(proposals, dtype=np.int64)
+        k = prop.shape[0]
+        if kind == "last_maximum":                 # ties go to the higher index
+            t = L.shape[1] - 1 - np.argmax(L[:, ::-1], axis=1)
+        else:
+            t = np.argmax(L, axis=1)
+        if kind == "row_shift":                    # draft r checked against the row after it
+            agree = [t[min(r + 1, k)] == prop[r] for r in range(k)]
+        else:
+            agree = [t[r] == prop[r] for r in range(k)]
+        if kind == "count_agreements":             # agreements anywhere, not the prefix
+            a = int(sum(agree))
+        else:
+            a = next((r for r in range(k) if not agree[r]), k)
+        if kind == "no_target_token":
+            committed = prop[:a]
+        elif kind == "target_token_of_last_row":
+            committed = np.concatenate([prop[:a], t[k:k + 1]])
+        else:
+            committed = np.concatenate([prop[:a], t[a:a + 1]])
+        return a, committed.astype(np.int32), t.astype(np.int32)
+    return greedy_accept
+
+
+def _accept_pins():
+    import test_oracle_accept as T
+    for k in (0, 1, 2, 3):
+        T.test_p10_brute_force_small_vocab_with_ties(k)
+    T.test_signed_zero_tie_takes_lower_index()
+    for a in (0, 7, 16):
+        T.test_planted_prefix_is_recovered(a)
+    T.test_exact_greedy_equivalence_on_a_toy_target()
+
+
+@pytest.mark.parametrize("kind", ["last_maximum", "row_shift", "count_agreements",
+                                  "no_target_token", "target_token_of_last_row"])
+def test_accept_pins_catch_planted_mistakes(kind, monkeypatch):
+    _accept_pins()
+    monkeypatch.setattr(oracle, "greedy_accept", _accept_mutant(kind))
+    with pytest.raises(AssertionError):
+        _accept_pins()
+
+
+def test_unmutated_accept_copy_passes_the_pins(monkeypatch):
+    """The copy the mutants start from is itself correct (so each mutant differs by one mistake)."""
+    monkeypatch.setattr(oracle, "greedy_accept", _accept_mutant("none"))
+    _accept_pins()
+    monkeypatch.setattr(oracle, "lse_merge", _merge_mutant("none"))
+    _merge_pins()
