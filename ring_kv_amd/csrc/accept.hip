@@ -92,11 +92,14 @@ __global__ __launch_bounds__(256) void accept_final_kernel(AcceptArgs a) {
   __shared__ int acc_len;
   const int tid = threadIdx.x;
   const int n_draft = a.n_rows - 1;
-  if (tid < n_draft) prop[tid] = a.proposals[tid];
+  // the draft token is loaded with the parts and written to LDS after them, so that its load
+  // does not hold the part loads back by a round trip
+  const int my_prop = n_draft > 0 ? a.proposals[min(tid, n_draft - 1)] : 0;   // clamped: in range
   int GP = 1;
   while (GP < a.parts && GP < 64) GP <<= 1;
   const int rpr = 256 / GP;                 // rows per round
   const int lg = tid % GP;                  // this lane's place in its row's group
+  const bool more_parts = a.parts > GP;     // vocabularies above 64 x 4,096 only
   for (int r0 = 0; r0 < a.n_rows; r0 += rpr * kRounds) {
     float lv[kRounds];
     int li[kRounds];
@@ -110,11 +113,11 @@ __global__ __launch_bounds__(256) void accept_final_kernel(AcceptArgs a) {
 #pragma unroll
     for (int k = 0; k < kRounds; ++k) {
       const int row = r0 + k * rpr + tid / GP;
-      float bv = -INFINITY;
-      int bi = INT_MAX;
-      if (row < a.n_rows && lg < a.parts && better(lv[k], li[k], bv, bi)) { bv = lv[k]; bi = li[k]; }
-      // parts beyond the first 64 (vocabularies above 64 x 4,096)
-      if (row < a.n_rows) {
+      // selects rather than a branch, so that the loads above stay ahead of every compare
+      const bool own = row < a.n_rows && lg < a.parts;
+      float bv = own ? lv[k] : -INFINITY;
+      int bi = own ? li[k] : INT_MAX;
+      if (more_parts && row < a.n_rows) {
         for (int p = lg + GP; p < a.parts; p += GP) {
           const float v = a.part_val[(int64_t)row * a.parts + p];
           const int i = a.part_idx[(int64_t)row * a.parts + p];
@@ -133,6 +136,7 @@ __global__ __launch_bounds__(256) void accept_final_kernel(AcceptArgs a) {
       }
     }
   }
+  if (tid < n_draft) prop[tid] = my_prop;
   __syncthreads();
   if (tid == 0) {
     int acc = n_draft;

@@ -76,3 +76,35 @@ def test_random_rows_against_the_oracle():
         prop = np.argmax(L, axis=1)[:16].astype(np.int32)
         prop[int(g.integers(0, 16))] = int(g.integers(0, vocab))
         _check(L, prop, f"random {trial}")
+
+
+@pytest.mark.parametrize("vocab", [262145, 300001, 1000003])
+def test_more_than_64_parts(vocab):
+    """Vocabularies above 64 parts of 4,096 logits, where each lane of a row's group also walks
+    the parts past the first 64: maxima planted on both sides of part 64 and at the ragged end,
+    and exact ties across it (the lower index wins)."""
+    g = np.random.default_rng(24)
+    L = g.standard_normal((17, vocab)).astype(np.float32)
+    spots = [0, 4095, 4096, 262143, 262144, vocab - 2, vocab - 1]
+    for r in range(17):
+        L[r, spots[r % len(spots)]] = np.float32(9.0)
+    L[7, [262144, vocab - 1]] = np.float32(11.0)        # tie past part 64: the lower wins
+    L[8, [5, vocab - 1]] = np.float32(11.0)             # tie across part 64
+    L[9, [262143, 262144]] = np.float32(11.0)           # tie straddling the part-64 boundary
+    prop = np.argmax(L, axis=1)[:16].astype(np.int32)
+    prop[12] = (prop[12] + 1) % vocab                   # disagreement at 12
+    say(f"accept more than 64 parts vocab={vocab}")
+    assert _check(L, prop, f"parts>64 {vocab}") == 12
+
+
+def test_many_rows_many_parts():
+    """255 drafts (256 rows, the most one call takes) at 38 parts per row: sixteen rounds of the
+    final reduction's row groups."""
+    g = np.random.default_rng(25)
+    vocab = 151936
+    L = g.standard_normal((256, vocab)).astype(np.float32)
+    t = np.argmax(L, axis=1)
+    prop = t[:255].astype(np.int32).copy()
+    prop[200] = (prop[200] + 3) % vocab
+    say("accept 256 rows x 151936")
+    assert _check(L, prop, "256x151936") == 200
