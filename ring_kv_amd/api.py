@@ -21,19 +21,31 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _need(t: torch.Tensor, name: str, dtype=None, ndim=None, device=None):
+def _form(t, name: str, dtype=None, shape=None):
+    """Type, dtype, contiguity and shape of one tensor argument; None in `shape` matches any
+    size.  The library takes plain pointers and trusts the sizes it is given, so every buffer
+    it reads or writes is checked here against the sizes the call will use."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
-    if device is not None and t.device != device:
-        raise ValueError(f"{name} is on {t.device}, expected {device}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and (t.dim() != len(shape) or
+                              any(e is not None and n != e for n, e in zip(t.shape, shape))):
+        want = "[" + "][".join("*" if e is None else str(e) for e in shape) + "]"
+        raise ValueError(f"{name} has shape {list(t.shape)}, expected {want}")
     if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
         raise ValueError(f"{name} has dtype {t.dtype}")
-    if ndim is not None and t.dim() != ndim:
-        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _on(device, **tensors):
+    """Every given tensor (None skipped) is a device tensor on `device`."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
 def _stream(stream, device):
@@ -52,44 +64,60 @@ def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
     if nbytes == 0:
         return None, 0
     if ws is not None:
+        _form(ws, "workspace")
+        _on(device, workspace=ws)
         if ws.numel() * ws.element_size() < nbytes:
             raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, need {nbytes}")
         return ws, ws.numel() * ws.element_size()
     return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
 
 
-def _outputs(q, out, lse, want_lse):
-    q_len, hq, d = q.shape
+def _outputs(q_len: int, hq: int, d: int, device, out, lse, want_lse):
     if out is None:
-        out = torch.empty((q_len, hq, d), dtype=torch.float32, device=q.device)
+        out = torch.empty((q_len, hq, d), dtype=torch.float32, device=device)
     if lse is None and want_lse:
-        lse = torch.empty((q_len, hq), dtype=torch.float32, device=q.device)
-    _need(out, "out", torch.float32, 3, q.device)
+        lse = torch.empty((q_len, hq), dtype=torch.float32, device=device)
+    _form(out, "out", torch.float32, (q_len, hq, d))
     if lse is not None:
-        _need(lse, "lse", torch.float32, 2, q.device)
+        _form(lse, "lse", torch.float32, (q_len, hq))
+    _on(device, out=out, lse=lse)
     return out, lse
+
+
+def _chunked(k, v, kname: str, vname: str, d: Optional[int] = None, n_kv: Optional[int] = None):
+    """A chunked K/V store: K [slots][Hkv][64][D] and V [slots][Hkv][D][64] bf16 of matching
+    sizes.  Returns (slots, Hkv, D)."""
+    _form(k, kname, torch.bfloat16, (None, n_kv, CHUNK, d))
+    n, hkv, _, dk = k.shape
+    _form(v, vname, torch.bfloat16, (n, hkv, dk, CHUNK))
+    return n, hkv, dk
+
+
+def _rows_pair(k, v, kname: str, vname: str):
+    """Rows K, V [n][Hkv][D] bf16 of the same shape.  Returns (n, Hkv, D)."""
+    _form(k, kname, torch.bfloat16, (None, None, None))
+    _form(v, vname, torch.bfloat16, tuple(k.shape))
+    return tuple(k.shape)
 
 
 def verify_attn_paged(q, k_pool, v_pool, page_table, ctx_len: int, *, num_splits: int = 0,
                       scale: float = 0.0, out=None, lse=None, want_lse: bool = True,
                       workspace=None, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Full-attention verify block over the paged pool of 64-token chunks."""
-    _need(q, "q", torch.bfloat16, 3)
+    _form(q, "q", torch.bfloat16, (None, None, None))
+    q_len, hq, d = q.shape
+    n_slots, hkv, _ = _chunked(k_pool, v_pool, "k_pool", "v_pool", d)
+    _form(page_table, "page_table", torch.int32, (None,))
     dev = q.device
-    _need(k_pool, "k_pool", torch.bfloat16, 4, dev)
-    _need(v_pool, "v_pool", torch.bfloat16, 4, dev)
-    _need(page_table, "page_table", torch.int32, 1, dev)
-    n_slots, hkv, chunk, d = k_pool.shape
-    if tuple(v_pool.shape) != (n_slots, hkv, d, chunk):
-        raise ValueError("v_pool must be [slots][Hkv][D][64]")
+    out, lse = _outputs(q_len, hq, d, dev, out, lse, want_lse)
+    _on(dev, q=q, k_pool=k_pool, v_pool=v_pool, page_table=page_table)
     dims = _dims(q, hkv, scale)
     L = lib()
-    ws, wsb = _workspace(L.verify_attn_paged_workspace_bytes(ctypes.byref(dims), ctx_len, chunk,
+    ws, wsb = _workspace(L.verify_attn_paged_workspace_bytes(ctypes.byref(dims), ctx_len, CHUNK,
                                                              num_splits), dev, workspace)
-    out, lse = _outputs(q, out, lse, want_lse)
     check("verify_attn_paged", L.verify_attn_paged(
         ctypes.byref(dims), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
-        page_table.numel(), n_slots, chunk, ctx_len, num_splits, _ptr(ws), wsb, _ptr(out),
+        page_table.numel(), n_slots, CHUNK, ctx_len, num_splits, _ptr(ws), wsb, _ptr(out),
         _ptr(lse), _stream(stream, dev)))
     return out, lse
 
@@ -104,24 +132,26 @@ def verify_attn_paged_partial(q, k_pool, v_pool, page_table, ctx_len: int, num_s
                               scale: float = 0.0, part_out=None, part_lse=None, stream=None):
     """Phase one of the paged call: per split of the chunk range, the normalised output
     [Hkv][S][rows][D] and the split's lse [Hkv][S][rows]."""
-    _need(q, "q", torch.bfloat16, 3)
-    dev = q.device
-    n_slots, hkv, chunk, d = k_pool.shape
-    q_len, hq, _ = q.shape
+    _form(q, "q", torch.bfloat16, (None, None, None))
+    q_len, hq, d = q.shape
+    n_slots, hkv, _ = _chunked(k_pool, v_pool, "k_pool", "v_pool", d)
+    _form(page_table, "page_table", torch.int32, (None,))
+    if num_splits < 1 or hq % hkv != 0:
+        raise ValueError("num_splits must be >= 1 and n_q_heads a multiple of n_kv_heads")
     rows = q_len * (hq // hkv)
+    dev = q.device
     if part_out is None:
         part_out = torch.empty((hkv, num_splits, rows, d), dtype=torch.float32, device=dev)
     if part_lse is None:
         part_lse = torch.empty((hkv, num_splits, rows), dtype=torch.float32, device=dev)
-    for t, n in ((k_pool, "k_pool"), (v_pool, "v_pool")):
-        _need(t, n, torch.bfloat16, 4, dev)
-    _need(page_table, "page_table", torch.int32, 1, dev)
-    _need(part_out, "part_out", torch.float32, 4, dev)
-    _need(part_lse, "part_lse", torch.float32, 3, dev)
+    _form(part_out, "part_out", torch.float32, (hkv, num_splits, rows, d))
+    _form(part_lse, "part_lse", torch.float32, (hkv, num_splits, rows))
+    _on(dev, q=q, k_pool=k_pool, v_pool=v_pool, page_table=page_table, part_out=part_out,
+        part_lse=part_lse)
     dims = _dims(q, hkv, scale)
     check("verify_attn_paged_partial", lib().verify_attn_paged_partial(
         ctypes.byref(dims), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
-        page_table.numel(), n_slots, chunk, ctx_len, num_splits, _ptr(part_out), _ptr(part_lse),
+        page_table.numel(), n_slots, CHUNK, ctx_len, num_splits, _ptr(part_out), _ptr(part_lse),
         _stream(stream, dev)))
     return part_out, part_lse
 
@@ -129,15 +159,16 @@ def verify_attn_paged_partial(q, k_pool, v_pool, page_table, ctx_len: int, num_s
 def attn_merge_partials(part_out, part_lse, q_len: int, n_q_heads: int, *, out=None, lse=None,
                         want_lse: bool = True, stream=None):
     """Log-sum-exp merge of split partials (layout of verify_attn_paged_partial)."""
-    _need(part_out, "part_out", torch.float32, 4)
-    dev = part_out.device
-    _need(part_lse, "part_lse", torch.float32, 3, dev)
+    _form(part_out, "part_out", torch.float32, (None, None, None, None))
     hkv, S, rows, d = part_out.shape
+    _form(part_lse, "part_lse", torch.float32, (hkv, S, rows))
+    if n_q_heads % hkv != 0 or rows != q_len * (n_q_heads // hkv):
+        raise ValueError(f"partials of {rows} rows per KV head do not match q_len {q_len} x "
+                         f"{n_q_heads} query heads over {hkv} KV heads")
+    dev = part_out.device
+    out, lse = _outputs(q_len, n_q_heads, d, dev, out, lse, want_lse)
+    _on(dev, part_out=part_out, part_lse=part_lse)
     dims = AttnDims(q_len, n_q_heads, hkv, d, 0.0, RKV_BF16)
-    if out is None:
-        out = torch.empty((q_len, n_q_heads, d), dtype=torch.float32, device=dev)
-    if lse is None and want_lse:
-        lse = torch.empty((q_len, n_q_heads), dtype=torch.float32, device=dev)
     check("attn_merge_partials", lib().attn_merge_partials(
         ctypes.byref(dims), S, _ptr(part_out), _ptr(part_lse), _ptr(out), _ptr(lse),
         _stream(stream, dev)))
@@ -148,19 +179,17 @@ def verify_attn_ring(q, k_ring, v_ring, pos0: int, window: int, *, num_splits: i
                      scale: float = 0.0, out=None, lse=None, want_lse: bool = True,
                      workspace=None, stream=None):
     """Sliding-window verify block over the position ring (slot = pos mod ring_size)."""
-    _need(q, "q", torch.bfloat16, 3)
+    _form(q, "q", torch.bfloat16, (None, None, None))
+    q_len, hq, d = q.shape
+    n_chunks, hkv, _ = _chunked(k_ring, v_ring, "k_ring", "v_ring", d)
     dev = q.device
-    _need(k_ring, "k_ring", torch.bfloat16, 4, dev)
-    _need(v_ring, "v_ring", torch.bfloat16, 4, dev)
-    n_chunks, hkv, chunk, d = k_ring.shape
-    if tuple(v_ring.shape) != (n_chunks, hkv, d, chunk):
-        raise ValueError("v_ring must be [ring/64][Hkv][D][64]")
-    ring_size = n_chunks * chunk
+    out, lse = _outputs(q_len, hq, d, dev, out, lse, want_lse)
+    _on(dev, q=q, k_ring=k_ring, v_ring=v_ring)
+    ring_size = n_chunks * CHUNK
     dims = _dims(q, hkv, scale)
     L = lib()
     ws, wsb = _workspace(L.verify_attn_ring_workspace_bytes(ctypes.byref(dims), ring_size, window,
                                                             num_splits), dev, workspace)
-    out, lse = _outputs(q, out, lse, want_lse)
     check("verify_attn_ring", L.verify_attn_ring(
         ctypes.byref(dims), _ptr(q), _ptr(k_ring), _ptr(v_ring), pos0, pos0 % ring_size,
         ring_size, window, num_splits, _ptr(ws), wsb, _ptr(out), _ptr(lse), _stream(stream, dev)))
@@ -171,18 +200,20 @@ def decode_attn_ref_layout(q, k, v, ctx_len: int, window: int = 0, *, num_splits
                            scale: float = 0.0, out=None, lse=None, want_lse: bool = True,
                            workspace=None, stream=None):
     """Verify/decode attention over the contiguous layout K, V [ctx][Hkv][D] (f32 or bf16)."""
-    _need(q, "q", (torch.float32, torch.bfloat16), 3)
-    dev = q.device
-    _need(k, "k", q.dtype, 3, dev)
-    _need(v, "v", q.dtype, 3, dev)
+    _form(q, "q", (torch.float32, torch.bfloat16), (None, None, None))
+    q_len, hq, d = q.shape
+    _form(k, "k", q.dtype, (None, None, d))
+    _form(v, "v", q.dtype, tuple(k.shape))
     hkv = k.shape[1]
-    if k.shape[0] < ctx_len or v.shape[0] < ctx_len:
+    if k.shape[0] < ctx_len:
         raise ValueError("k, v hold fewer than ctx_len rows")
+    dev = q.device
+    out, lse = _outputs(q_len, hq, d, dev, out, lse, want_lse)
+    _on(dev, q=q, k=k, v=v)
     dims = _dims(q, hkv, scale)
     L = lib()
     ws, wsb = _workspace(L.decode_attn_ref_layout_workspace_bytes(ctypes.byref(dims), ctx_len,
                                                                   num_splits), dev, workspace)
-    out, lse = _outputs(q, out, lse, want_lse)
     check("decode_attn_ref_layout", L.decode_attn_ref_layout(
         ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), ctx_len, window, num_splits, _ptr(ws), wsb,
         _ptr(out), _ptr(lse), _stream(stream, dev)))
@@ -192,19 +223,23 @@ def decode_attn_ref_layout(q, k, v, ctx_len: int, window: int = 0, *, num_splits
 def verify_accept(logits, proposals, *, accept_len=None, committed=None, row_argmax=None,
                   want_argmax: bool = True, workspace=None, stream=None):
     """Greedy acceptance: (accept_len [1], committed [k+1] (-1 after a+1), row_argmax [k+1])."""
-    _need(logits, "logits", torch.float32, 2)
-    dev = logits.device
-    _need(proposals, "proposals", torch.int32, 1, dev)
+    _form(proposals, "proposals", torch.int32, (None,))
     k = proposals.numel()
-    if logits.shape[0] != k + 1:
-        raise ValueError("need k+1 logit rows for k proposals")
+    _form(logits, "logits", torch.float32, (k + 1, None))
     vocab = logits.shape[1]
+    dev = logits.device
     if accept_len is None:
         accept_len = torch.empty(1, dtype=torch.int32, device=dev)
     if committed is None:
         committed = torch.empty(k + 1, dtype=torch.int32, device=dev)
     if row_argmax is None and want_argmax:
         row_argmax = torch.empty(k + 1, dtype=torch.int32, device=dev)
+    _form(accept_len, "accept_len", torch.int32, (1,))
+    _form(committed, "committed", torch.int32, (k + 1,))
+    if row_argmax is not None:
+        _form(row_argmax, "row_argmax", torch.int32, (k + 1,))
+    _on(dev, logits=logits, proposals=proposals, accept_len=accept_len, committed=committed,
+        row_argmax=row_argmax)
     L = lib()
     ws, wsb = _workspace(L.verify_accept_workspace_bytes(k, vocab), dev, workspace)
     check("verify_accept", L.verify_accept(
@@ -215,29 +250,26 @@ def verify_accept(logits, proposals, *, accept_len=None, committed=None, row_arg
 
 def ref_layout_to_ring(k_src, v_src, pos_first: int, k_ring, v_ring, *, stream=None):
     """Write rows k_src, v_src [n][Hkv][D] (positions pos_first..) into the ring."""
-    _need(k_src, "k_src", torch.bfloat16, 3)
+    n, hkv, d = _rows_pair(k_src, v_src, "k_src", "v_src")
+    n_chunks, _, _ = _chunked(k_ring, v_ring, "k_ring", "v_ring", d, hkv)
     dev = k_src.device
-    for t, n in ((v_src, "v_src"), (k_ring, "k_ring"), (v_ring, "v_ring")):
-        _need(t, n, torch.bfloat16, None, dev)
-    n, hkv, d = k_src.shape
-    ring_size = k_ring.shape[0] * CHUNK
+    _on(dev, k_src=k_src, v_src=v_src, k_ring=k_ring, v_ring=v_ring)
     check("ref_layout_to_ring", lib().ref_layout_to_ring(
         _ptr(k_src), _ptr(v_src), pos_first, n, hkv, d, RKV_BF16, _ptr(k_ring), _ptr(v_ring),
-        ring_size, _stream(stream, dev)))
+        n_chunks * CHUNK, _stream(stream, dev)))
 
 
 def ref_layout_to_paged(k_src, v_src, pos_first: int, k_pool, v_pool, page_table, *,
                         stream=None):
     """Write rows k_src, v_src [n][Hkv][D] (positions pos_first..) into the paged pool."""
-    _need(k_src, "k_src", torch.bfloat16, 3)
+    n, hkv, d = _rows_pair(k_src, v_src, "k_src", "v_src")
+    n_slots, _, _ = _chunked(k_pool, v_pool, "k_pool", "v_pool", d, hkv)
+    _form(page_table, "page_table", torch.int32, (None,))
     dev = k_src.device
-    for t, n in ((v_src, "v_src"), (k_pool, "k_pool"), (v_pool, "v_pool")):
-        _need(t, n, torch.bfloat16, None, dev)
-    _need(page_table, "page_table", torch.int32, 1, dev)
-    n, hkv, d = k_src.shape
+    _on(dev, k_src=k_src, v_src=v_src, k_pool=k_pool, v_pool=v_pool, page_table=page_table)
     check("ref_layout_to_paged", lib().ref_layout_to_paged(
         _ptr(k_src), _ptr(v_src), pos_first, n, hkv, d, RKV_BF16, _ptr(k_pool), _ptr(v_pool),
-        _ptr(page_table), page_table.numel(), k_pool.shape[0], CHUNK, _stream(stream, dev)))
+        _ptr(page_table), page_table.numel(), n_slots, CHUNK, _stream(stream, dev)))
 
 
 class Pager:
@@ -316,50 +348,49 @@ class Pager:
 def verify_kv_append_ring(k_new, v_new, pos_first: int, k_ring, v_ring, *, stream=None):
     """Append a verify block's rows k_new, v_new [n][Hkv][D] (positions pos_first..) to the
     ring at slot pos mod ring_size."""
-    _need(k_new, "k_new", torch.bfloat16, 3)
+    n, hkv, d = _rows_pair(k_new, v_new, "k_new", "v_new")
+    n_chunks, _, _ = _chunked(k_ring, v_ring, "k_ring", "v_ring", d, hkv)
     dev = k_new.device
-    for t, nm in ((v_new, "v_new"), (k_ring, "k_ring"), (v_ring, "v_ring")):
-        _need(t, nm, torch.bfloat16, 4 if nm != "v_new" else 3, dev)
-    n, hkv, d = k_new.shape
+    _on(dev, k_new=k_new, v_new=v_new, k_ring=k_ring, v_ring=v_ring)
     check("verify_kv_append_ring", lib().verify_kv_append_ring(
         _ptr(k_new), _ptr(v_new), n, pos_first, hkv, d, _ptr(k_ring), _ptr(v_ring),
-        k_ring.shape[0] * CHUNK, _stream(stream, dev)))
+        n_chunks * CHUNK, _stream(stream, dev)))
 
 
 def verify_kv_append_paged(k_new, v_new, ctx_len: int, k_pool, v_pool, page_table,
                            first_chunk: int, new_slots, *, stream=None):
     """Append a verify block's rows (positions ctx_len..) to the pool; the chunks the block
     starts (from Pager.reserve) get new_slots, written into the device page table too."""
-    _need(k_new, "k_new", torch.bfloat16, 3)
+    n, hkv, d = _rows_pair(k_new, v_new, "k_new", "v_new")
+    n_slots, _, _ = _chunked(k_pool, v_pool, "k_pool", "v_pool", d, hkv)
+    _form(page_table, "page_table", torch.int32, (None,))
     dev = k_new.device
-    for t, nm in ((v_new, "v_new"), (k_pool, "k_pool"), (v_pool, "v_pool")):
-        _need(t, nm, torch.bfloat16, 4 if nm != "v_new" else 3, dev)
-    _need(page_table, "page_table", torch.int32, 1, dev)
-    n, hkv, d = k_new.shape
+    _on(dev, k_new=k_new, v_new=v_new, k_pool=k_pool, v_pool=v_pool, page_table=page_table)
     slots = (ctypes.c_int32 * max(1, len(new_slots)))(*new_slots)
     check("verify_kv_append_paged", lib().verify_kv_append_paged(
         _ptr(k_new), _ptr(v_new), n, ctx_len, hkv, d, _ptr(k_pool), _ptr(v_pool),
-        _ptr(page_table), page_table.numel(), k_pool.shape[0], first_chunk, len(new_slots),
+        _ptr(page_table), page_table.numel(), n_slots, first_chunk, len(new_slots),
         slots, _stream(stream, dev)))
 
 
-def _host_store(t: torch.Tensor, name: str, ndim: int = 4):
-    if not isinstance(t, torch.Tensor) or t.is_cuda:
-        raise ValueError(f"{name} must be a host tensor (pinned for asynchronous copies)")
-    if not t.is_contiguous() or t.dtype != torch.bfloat16 or t.dim() != ndim:
-        raise ValueError(f"{name} must be a contiguous bf16 [chunks][Hkv][..][..] host tensor")
+def _host_stores(k_host, v_host, hkv: int, d: int) -> int:
+    """Host chunk stores laid out like the pool's slots: K [n_host][Hkv][64][D] and V
+    [n_host][Hkv][D][64] bf16 host tensors (pinned for asynchronous copies).  Returns n_host."""
+    for t, name in ((k_host, "k_host"), (v_host, "v_host")):
+        if not isinstance(t, torch.Tensor) or t.is_cuda:
+            raise ValueError(f"{name} must be a host tensor (pinned for asynchronous copies)")
+    _chunked(k_host, v_host, "k_host", "v_host", d, hkv)
+    return k_host.shape[0]
 
 
 def kv_page_out(k_pool, v_pool, slots, chunk_ids, k_host, v_host, *, workspace=None,
                 stream=None):
     """Copy pool slots[i] to host entries chunk_ids[i] (K and V, bit-exact), asynchronously on
     the stream; k_host [n_host][Hkv][64][D], v_host [n_host][Hkv][D][64] host tensors."""
-    _need(k_pool, "k_pool", torch.bfloat16, 4)
+    n_slots, hkv, d = _chunked(k_pool, v_pool, "k_pool", "v_pool")
+    n_host = _host_stores(k_host, v_host, hkv, d)
     dev = k_pool.device
-    _need(v_pool, "v_pool", torch.bfloat16, 4, dev)
-    _host_store(k_host, "k_host")
-    _host_store(v_host, "v_host")
-    n_slots, hkv, _, d = k_pool.shape
+    _on(dev, k_pool=k_pool, v_pool=v_pool)
     n = len(slots)
     if len(chunk_ids) != n:
         raise ValueError("slots and chunk_ids differ in length")
@@ -370,7 +401,7 @@ def kv_page_out(k_pool, v_pool, slots, chunk_ids, k_host, v_host, *, workspace=N
     check("kv_page_out", L.kv_page_out(
         _ptr(k_pool), _ptr(v_pool), hkv, d, n_slots, sl, ci, n,
         ctypes.c_void_p(k_host.data_ptr()), ctypes.c_void_p(v_host.data_ptr()),
-        k_host.shape[0], _ptr(ws), wsb, _stream(stream, dev)))
+        n_host, _ptr(ws), wsb, _stream(stream, dev)))
     return ws
 
 
@@ -378,12 +409,10 @@ def kv_page_in(k_host, v_host, chunk_ids, slots, k_pool, v_pool, *, workspace=No
                stream=None):
     """Copy host entries chunk_ids[i] into pool slots[i] (K and V, bit-exact), asynchronously
     on the stream."""
-    _need(k_pool, "k_pool", torch.bfloat16, 4)
+    n_slots, hkv, d = _chunked(k_pool, v_pool, "k_pool", "v_pool")
+    n_host = _host_stores(k_host, v_host, hkv, d)
     dev = k_pool.device
-    _need(v_pool, "v_pool", torch.bfloat16, 4, dev)
-    _host_store(k_host, "k_host")
-    _host_store(v_host, "v_host")
-    n_slots, hkv, _, d = k_pool.shape
+    _on(dev, k_pool=k_pool, v_pool=v_pool)
     n = len(slots)
     if len(chunk_ids) != n:
         raise ValueError("slots and chunk_ids differ in length")
@@ -392,7 +421,7 @@ def kv_page_in(k_host, v_host, chunk_ids, slots, k_pool, v_pool, *, workspace=No
     sl = (ctypes.c_int32 * max(1, n))(*slots)
     ci = (ctypes.c_int32 * max(1, n))(*chunk_ids)
     check("kv_page_in", L.kv_page_in(
-        ctypes.c_void_p(k_host.data_ptr()), ctypes.c_void_p(v_host.data_ptr()), k_host.shape[0],
+        ctypes.c_void_p(k_host.data_ptr()), ctypes.c_void_p(v_host.data_ptr()), n_host,
         ci, sl, n, _ptr(k_pool), _ptr(v_pool), hkv, d, n_slots, _ptr(ws), wsb,
         _stream(stream, dev)))
     return ws
@@ -403,21 +432,19 @@ def verify_attn_paged_resident(q, k_pool, v_pool, d_slots, chunk_ids, ctx_len: i
                                want_lse: bool = True, workspace=None, stream=None):
     """Full-attention attention of the block over the resident chunks only: chunk_ids (host
     list, increasing) read from the device slot list d_slots."""
-    _need(q, "q", torch.bfloat16, 3)
-    dev = q.device
-    _need(k_pool, "k_pool", torch.bfloat16, 4, dev)
-    _need(v_pool, "v_pool", torch.bfloat16, 4, dev)
-    _need(d_slots, "d_slots", torch.int32, 1, dev)
-    n_slots, hkv, chunk, d = k_pool.shape
+    _form(q, "q", torch.bfloat16, (None, None, None))
+    q_len, hq, d = q.shape
+    n_slots, hkv, _ = _chunked(k_pool, v_pool, "k_pool", "v_pool", d)
     n_res = len(chunk_ids)
-    if d_slots.numel() != n_res:
-        raise ValueError("d_slots and chunk_ids differ in length")
+    _form(d_slots, "d_slots", torch.int32, (n_res,))
+    dev = q.device
+    out, lse = _outputs(q_len, hq, d, dev, out, lse, want_lse)
+    _on(dev, q=q, k_pool=k_pool, v_pool=v_pool, d_slots=d_slots)
     dims = _dims(q, hkv, scale)
     L = lib()
     # the call runs over n_res chunks: its splits and workspace are those of 64 * n_res positions
-    ws, wsb = _workspace(L.verify_attn_paged_workspace_bytes(ctypes.byref(dims), chunk * n_res,
-                                                             chunk, num_splits), dev, workspace)
-    out, lse = _outputs(q, out, lse, want_lse)
+    ws, wsb = _workspace(L.verify_attn_paged_workspace_bytes(ctypes.byref(dims), CHUNK * n_res,
+                                                             CHUNK, num_splits), dev, workspace)
     ci = (ctypes.c_int32 * max(1, n_res))(*chunk_ids)
     check("verify_attn_paged_resident", L.verify_attn_paged_resident(
         ctypes.byref(dims), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(d_slots), ci, n_res,
