@@ -54,13 +54,17 @@ def to_f64(x, dtype: str) -> np.ndarray:
 
 
 def key_bounds(p: int, window: int):
-    """Inclusive range of key positions visible to a query at position ``p``."""
+    """Inclusive range of key positions visible to a query at position ``p``: all earlier
+    positions and its own, or the last ``window`` of them (lucebox post, "3. Ring caches for the
+    sliding-window layers": the 512-token window; W keys including the query's own)."""
     lo = max(0, p - window + 1) if window > 0 else 0
     return lo, p
 
 
 def attend_rows(q, k_of_head, v_of_head, key_pos, q_pos, window, scale, n_kv_heads):
-    """Attention of the block over an explicit key list.
+    """Attention of the block over an explicit key list: the softmax definition above, for
+    the one batched forward over the proposals (lucebox post, "The model, fast MoE with a
+    drafter in the box").
 
     q          [q_len][Hq][D] float64
     k_of_head  callable g -> [n][D] float64: K(key_pos[j])[g] for every listed key
@@ -101,7 +105,9 @@ def _scale(scale, d):
 
 
 def attention_contiguous(q, k, v, ctx_len, window=0, scale=None, dtype="f64", q_len=None):
-    """Contiguous rows ``k, v [ctx][Hkv][D]``; query i at position ctx_len - q_len + i."""
+    """Contiguous rows ``k, v [ctx][Hkv][D]``; query i at position ctx_len - q_len + i (the
+    block counted in the context, as one batched forward over the proposals: lucebox post, "The
+    model, fast MoE with a drafter in the box")."""
     qf = to_f64(q, dtype)
     q_len = qf.shape[0] if q_len is None else q_len
     kf = to_f64(np.asarray(k)[:ctx_len], dtype)
@@ -116,7 +122,8 @@ def attention_contiguous(q, k, v, ctx_len, window=0, scale=None, dtype="f64", q_
 
 
 def gather_ring(k_ring, v_ring, positions, ring_size, chunk=CHUNK):
-    """K(j), V(j) for positions ``j`` read from the ring at slot j mod ring_size.
+    """K(j), V(j) for positions ``j`` read from the ring at slot j mod ring_size (lucebox post,
+    "3. Ring caches for the sliding-window layers": slot = pos mod 2048).
 
     Returns two callables g -> [n][D] (raw element type, not converted)."""
     positions = np.asarray(positions, dtype=np.int64)
@@ -128,7 +135,8 @@ def gather_ring(k_ring, v_ring, positions, ring_size, chunk=CHUNK):
 
 def attention_ring(q, k_ring, v_ring, pos0, ring_head, ring_size, window, scale=None,
                    dtype="bf16", chunk=CHUNK):
-    """Sliding-window verify attention over a position ring.
+    """Sliding-window verify attention over a position ring (lucebox post, "3. Ring caches for
+    the sliding-window layers").
 
     Query i sits at pos0 + i; the ring holds the last ``ring_size`` positions up to
     pos0 + q_len - 1 (the block's own rows included).  Raises if a visible position
@@ -154,7 +162,8 @@ def attention_ring(q, k_ring, v_ring, pos0, ring_head, ring_size, window, scale=
 
 
 def gather_paged(k_pool, v_pool, page_table, positions, chunk=CHUNK):
-    """K(j), V(j) for positions ``j`` read from pool slot page_table[j // chunk] at j % chunk."""
+    """K(j), V(j) for positions ``j`` read from pool slot page_table[j // chunk] at j % chunk
+    (lucebox post, "Three optimizations", item 1: the pool of 64-token chunks)."""
     positions = np.asarray(positions, dtype=np.int64)
     pt = np.asarray(page_table, dtype=np.int64)
     slot = pt[positions // chunk]
@@ -165,8 +174,9 @@ def gather_paged(k_pool, v_pool, page_table, positions, chunk=CHUNK):
 
 def attention_paged(q, k_pool, v_pool, page_table, ctx_len, scale=None, dtype="bf16",
                     chunk=CHUNK, window=0):
-    """Full-attention (or windowed) verify attention over the paged pool.  Keys are
-    positions 0 .. ctx_len-1; query i sits at ctx_len - q_len + i."""
+    """Full-attention (or windowed) verify attention over the paged pool (lucebox post,
+    "Three optimizations", item 1).  Keys are positions 0 .. ctx_len-1; query i sits at
+    ctx_len - q_len + i."""
     qf = to_f64(q, dtype)
     q_len = qf.shape[0]
     n_chunks = -(-ctx_len // chunk)

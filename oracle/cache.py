@@ -46,7 +46,8 @@ PAGED_OUT = -2
 
 
 def append_ring(k_ring, v_ring, k_new, v_new, pos_first: int):
-    """Rows k_new, v_new [n][Hkv][D] (positions pos_first ..) written at slot pos mod R."""
+    """Rows k_new, v_new [n][Hkv][D] (positions pos_first ..) written at slot pos mod R (lucebox
+    post, "3. Ring caches for the sliding-window layers")."""
     k = np.array(k_ring, copy=True)
     v = np.array(v_ring, copy=True)
     ring = k.shape[0] * CHUNK
@@ -60,7 +61,7 @@ def append_ring(k_ring, v_ring, k_new, v_new, pos_first: int):
 
 def append_paged(k_pool, v_pool, table, k_new, v_new, pos_first: int):
     """Rows written at slot table[pos // 64], offset pos % 64 (the table already holds the
-    slots of the chunks the rows fall in)."""
+    slots of the chunks the rows fall in; lucebox post, "Three optimizations", item 1)."""
     k = np.array(k_pool, copy=True)
     v = np.array(v_pool, copy=True)
     for i in range(k_new.shape[0]):
@@ -73,7 +74,8 @@ def append_paged(k_pool, v_pool, table, k_new, v_new, pos_first: int):
 
 
 def page_out(k_pool, v_pool, slots, chunk_ids, k_host, v_host):
-    """Host entries chunk_ids[i] <- pool slot slots[i] (K and V).  Returns the new host stores."""
+    """Host entries chunk_ids[i] <- pool slot slots[i] (K and V), bit for bit (lucebox post,
+    "Three optimizations", item 1: cold chunks page to host RAM).  Returns the new host stores."""
     kh = np.array(k_host, copy=True)
     vh = np.array(v_host, copy=True)
     for s, c in zip(slots, chunk_ids):
@@ -83,7 +85,8 @@ def page_out(k_pool, v_pool, slots, chunk_ids, k_host, v_host):
 
 
 def page_in(k_host, v_host, chunk_ids, slots, k_pool, v_pool):
-    """Pool slots slots[i] <- host entries chunk_ids[i] (K and V).  Returns the new pool."""
+    """Pool slots slots[i] <- host entries chunk_ids[i] (K and V), bit for bit (same passage).
+    Returns the new pool."""
     kp = np.array(k_pool, copy=True)
     vp = np.array(v_pool, copy=True)
     for c, s in zip(chunk_ids, slots):
@@ -93,7 +96,8 @@ def page_in(k_host, v_host, chunk_ids, slots, k_pool, v_pool):
 
 
 def attention_resident(q, k_pool, v_pool, chunk_ids, slots, ctx_len, scale=None, dtype="bf16"):
-    """Attention of the block over the resident chunks only: the keys are positions
+    """Attention of the block over the resident chunks only (lucebox post, "Three optimizations",
+    item 1: only part of the context stays in the pool): the keys are positions
     c*64 .. c*64+63 (below ctx_len) of every listed chunk c, read from pool slot slots[i]; query
     i sits at ctx_len - q_len + i and sees the listed keys at or before its own position."""
     qf = to_f64(q, dtype)
@@ -115,7 +119,10 @@ def attention_resident(q, k_pool, v_pool, chunk_ids, slots, ctx_len, scale=None,
 
 
 class PagerModel:
-    """Slot bookkeeping of one sequence's pool chunks: committed length, table, free stack."""
+    """Slot bookkeeping of one sequence's pool chunks: committed length, table, free stack
+    (lucebox post, "Three optimizations", item 1 for the chunk pool; "The model, fast MoE with a
+    drafter in the box" for committing only the target's own tokens; the allocation policy is
+    a reading, stated above)."""
 
     def __init__(self, n_slots: int, n_table: int):
         self.table = [-1] * n_table

@@ -20,12 +20,14 @@ from .attention import attend_rows
 
 
 def attention_partial(q, k_of_head, v_of_head, key_pos, q_pos, window, scale, n_kv_heads):
-    """Attention restricted to the listed keys (one part of a split)."""
+    """Attention restricted to the listed keys (one part of a split of the key range; the pages
+    describe no split, so the part boundaries are the caller's)."""
     return attend_rows(q, k_of_head, v_of_head, key_pos, q_pos, window, scale, n_kv_heads)
 
 
 def lse_merge(parts):
-    """Merge ``[(O_s, lse_s), ...]`` over disjoint key parts (shapes [..., D] and [...])."""
+    """Merge ``[(O_s, lse_s), ...]`` over disjoint key parts (shapes [..., D] and [...]): the
+    regrouping of one softmax over the union stated above, exact up to rounding."""
     lses = np.stack([np.asarray(l, dtype=np.float64) for _, l in parts])      # [S, ...]
     outs = np.stack([np.asarray(o, dtype=np.float64) for o, _ in parts])      # [S, ..., D]
     M = lses.max(axis=0)
