@@ -2,7 +2,10 @@
 // bf16 inputs, every arithmetic step in f32: the products on the f32 matrix cores
 // (v_mfma_f32_16x16x4_f32), the softmax on the vector ALUs.  It is the GPU-side reference the
 // chunked stores are checked against (and plain decode with one query); the HBM-bound verify
-// path is the bf16 MFMA kernel over the chunked stores.
+// path is the bf16 MFMA kernel over the chunked stores.  Query i of the block sees the
+// block's earlier tokens and itself (lucebox post "Laguna XS 2.1 33B on a RTX 3090: 296 tok/s
+// peak, 152 tok/s at 256K context", "The model, fast MoE with a drafter in the box": the
+// proposals are scored in one batched forward).
 //
 // Workgroup = (KV head, split of whole 64-key tiles, tile of 64 rows); wave w owns rows
 // 16w .. 16w+15.  Per 64-key tile, staged in LDS as f32:

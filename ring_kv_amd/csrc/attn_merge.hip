@@ -2,6 +2,8 @@
 // output O_s and lse_s over its own keys; with M = max_s lse_s and w_s = exp(lse_s - M) the
 // whole is sum_s w_s O_s / sum_s w_s and lse = M + ln sum_s w_s (a regrouping of the plain
 // softmax over all keys; splits with lse_s = -inf saw no key of a row and carry no weight).
+// The pages split no key range; the split over chunk ranges is this library's way of spreading
+// one long-context verify block over all compute units.
 #include "rkv_device.hpp"
 #include "rkv_launch.hpp"
 
