@@ -94,6 +94,13 @@ def graph_ms(fn, inner, reps, torch):
     return event_ms(g.replay, reps, torch) / inner
 
 
+def median_graph_us(fn, reps, torch, rounds=3):
+    """µs per call: the median of `rounds` graph measurements of two calls each (the matrix-core
+    kernels' clock moves with the card's power draw, by up to ~8% between rounds)."""
+    import statistics
+    return statistics.median(graph_ms(fn, 2, reps, torch) for _ in range(rounds)) * 1e3
+
+
 def event_ms(fn, n, torch):
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -425,7 +432,7 @@ def prefill_timings(torch, rk, synth, reps):
                 pl = torch.empty((4, S, rows), dtype=torch.float32, device="cuda")
                 part = lambda: rk.verify_attn_paged_partial(q, kp, vp, pt, c.ctx_len, S,  # noqa: E731
                                                             part_out=po, part_lse=pl)
-                k_us = graph_ms(part, 2, reps, torch) * 1e3
+                k_us = median_graph_us(part, reps, torch)
                 tf = flops / (k_us * 1e-6) / 1e12
                 out["roofline_mfma"] = {
                     "bound": "mfma",
@@ -433,7 +440,7 @@ def prefill_timings(torch, rk, synth, reps):
                     "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "us_per_launch": round(k_us, 1),
                     "algorithmic_flops_per_launch": flops, "traffic": None}
-        us = graph_ms(fn, 2, reps, torch) * 1e3
+        us = median_graph_us(fn, reps, torch)
         tf = flops / (us * 1e-6) / 1e12
         e.update({"us": round(us, 1), "tflops": round(tf, 1),
                   "util_mfma_bf16": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
