@@ -422,13 +422,17 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
     for (int j = 0; j < NST; ++j)
       first[j] = paged ? a.pt[c_lo + min(j, nloc - 1)] : slot_of(j);
     // ---- page-table slice in LDS: entry for local chunk loc at pt_lds[loc % kPtCap] ---
-    // One entry per thread for the first kPtCap chunks; splits longer than that refresh one
-    // half of the slice at a time, 128 chunks before it is needed (and always take the
-    // masking path, as their later entries are not checked here).
-    static_assert(NT == kPtCap, "one table entry per thread");
-    const bool tload = paged && tid < nloc;
-    int tval = 0;
-    if (tload) tval = a.pt[c_lo + tid];
+    // kPtCap / NT entries per thread for the first kPtCap chunks; splits longer than that
+    // refresh one half of the slice at a time, 128 chunks before it is needed (and always take
+    // the masking path, as their later entries are not checked here).
+    constexpr int TPT = kPtCap / NT;
+    static_assert(kPtCap % NT == 0, "whole table entries per thread");
+    int tval[TPT];
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) {
+      const int e = tid + j * NT;
+      tval[j] = (paged && e < nloc) ? a.pt[c_lo + e] : 0;
+    }
     load_q();
 
     // ---- pipeline: NST chunks in flight in registers while one is computed -------------
@@ -449,8 +453,15 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
     if (paged) {
-      if (tload) pt_lds[tid] = tval;
-      const bool bad = tload && (unsigned)tval >= (unsigned)a.n_slots;
+      bool bad = false;
+#pragma unroll
+      for (int j = 0; j < TPT; ++j) {
+        const int e = tid + j * NT;
+        if (e < nloc) {
+          pt_lds[e] = tval[j];
+          bad |= (unsigned)tval[j] >= (unsigned)a.n_slots;
+        }
+      }
       if (lane == 0) wave_flag[w] = __builtin_amdgcn_ballot_w64(bad) != 0;
     }
     // Q has arrived before the loop: left pending, the wait-count analysis would merge its
@@ -606,9 +617,15 @@ hipError_t launch_t(const ChunkAttnArgs& a, hipStream_t stream) {
 
 // Tiles of 64 rows (blockIdx.y), two waves per row group (key halves).  Tiles of one split
 // each read its chunks; a variant with more row groups per workgroup would need more registers
-// than the register stages leave.
+// than the register stages leave.  Where 64-row tiles would leave most of the chip without a
+// workgroup (a window layer's 40, a short pool context's 128), tiles of 32 rows (two row groups,
+// four waves) double the workgroups and halve each one's arithmetic per chunk; the tiles of one
+// split read the same chunks, the second time from cache.
 template <int D>
 hipError_t launch_d(const ChunkAttnArgs& a, hipStream_t stream) {
+  const int rows = a.q_len * a.G;
+  const int64_t wgs = (int64_t)a.n_kv_heads * a.num_splits * ((rows + 63) / 64);
+  if (wgs < kVerifyFillWorkgroups) return launch_t<D, 2, 2>(a, stream);
   return launch_t<D, 4, 2>(a, stream);
 }
 
