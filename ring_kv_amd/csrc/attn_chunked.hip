@@ -617,15 +617,19 @@ hipError_t launch_t(const ChunkAttnArgs& a, hipStream_t stream) {
 
 // Tiles of 64 rows (blockIdx.y), two waves per row group (key halves).  Tiles of one split
 // each read its chunks; a variant with more row groups per workgroup would need more registers
-// than the register stages leave.  Where 64-row tiles would leave most of the chip without a
-// workgroup (a window layer's 40, a short pool context's 128), tiles of 32 rows (two row groups,
-// four waves) double the workgroups and halve each one's arithmetic per chunk; the tiles of one
-// split read the same chunks, the second time from cache.
+// than the register stages leave.  The tile is the smallest of 16, 32 and 64 rows whose grid
+// still fits one round of one workgroup per compute unit (a smaller tile's workgroup takes a
+// whole unit too, by its registers): a window layer runs 160 workgroups of 16 rows instead of
+// 40 of 64, a pool context of 8,192 256 of 32 rows instead of 128; smaller tiles divide each
+// workgroup's arithmetic per chunk, and the tiles of one split read the same chunks, after the
+// first time from cache.  A grid of 132 workgroups keeps 64 rows (264 would take two rounds),
+// and the long contexts keep them too, their 256 workgroups already filling the chip.
 template <int D>
 hipError_t launch_d(const ChunkAttnArgs& a, hipStream_t stream) {
   const int rows = a.q_len * a.G;
   const int64_t wgs = (int64_t)a.n_kv_heads * a.num_splits * ((rows + 63) / 64);
-  if (wgs < kVerifyFillWorkgroups) return launch_t<D, 2, 2>(a, stream);
+  if (4 * wgs <= kVerifyFillWorkgroups) return launch_t<D, 1, 2>(a, stream);
+  if (2 * wgs <= kVerifyFillWorkgroups) return launch_t<D, 2, 2>(a, stream);
   return launch_t<D, 4, 2>(a, stream);
 }
 

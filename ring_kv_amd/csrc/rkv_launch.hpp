@@ -38,7 +38,8 @@ struct ChunkAttnArgs {
 // HBM-streaming kernel with 64-row tiles; longer blocks (batched prefill) run the matrix-core
 // kernel with tiles of kPrefillTileRows rows.  launch_chunk_attn picks the kernel.
 constexpr int kVerifyMaxRows = 256;
-// A verify launch of fewer 64-row workgroups than this takes 32-row tiles instead.
+// One round of verify workgroups (one per compute unit): the row tile is the smallest whose grid
+// fits it.
 constexpr int kVerifyFillWorkgroups = 256;
 constexpr int kPrefillTileRows = 256;
 // Row tile of the prefill kernel: kPrefillTileRows, or half of it (two waves per row group, one
