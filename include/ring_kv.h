@@ -70,7 +70,7 @@ extern "C" {
  * (16 drafts: 64 rows at G = 4) and a batched prefill block (lucebox post, "TL;DR": prefill
  * as pooled batches plus ring attention; 1024 tokens: 4096 rows at G = 4) go through the same
  * calls.  Up to 256 rows the chunked calls stream the KV with 64-row tiles; longer blocks run a
- * matrix-core kernel with 128- or 256-row tiles.  Same definition, layouts and results. */
+ * matrix-core kernel with 64-, 128- or 256-row tiles.  Same definition, layouts and results. */
 #define RKV_MAX_ROWS 16384
 
 typedef enum rkv_status {

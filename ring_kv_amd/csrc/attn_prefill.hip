@@ -16,8 +16,9 @@
 //     O^T [D x 32 rows]     += V^T [D x 64] . P^T         (D/32) x 4 MFMA 32x32x16 bf16
 //   (half of each with KS = 2, whose two halves merge their softmax states at the end).
 //   256-row tiles give every K/V element staged in LDS the most reuse; 128-row tiles (KS = 2)
-//   double the workgroups of a block whose 256-row grid leaves most of the chip idle (a block
-//   over the ring, where each tile sees only its window and is not split).
+//   double the workgroups of a block whose 256-row grid leaves most of the chip idle, and
+//   64-row tiles (two row groups, KS = 2) quadruple them where that grid still fits one round
+//   (a block over the ring, where each tile sees only its window and is not split).
 //
 // S is computed transposed so that each lane ends with 16 scores of ONE row per 32-key tile,
 // which after a fixed permutation of the keys (rho below) is exactly the B operand of P^T for
@@ -480,9 +481,10 @@ hipError_t launch_t(const ChunkAttnArgs& a, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_d(const ChunkAttnArgs& a, hipStream_t stream) {
-  if (prefill_tile_rows(a.q_len * a.G, a.n_kv_heads, a.num_splits) == kPrefillTileRows)
-    return launch_t<D, kPrefillTileRows / 32, 1>(a, stream);
-  return launch_t<D, kPrefillTileRows / 64, 2>(a, stream);
+  const int tile = prefill_tile_rows(a.q_len * a.G, a.n_kv_heads, a.num_splits);
+  if (tile == kPrefillTileRows) return launch_t<D, kPrefillTileRows / 32, 1>(a, stream);
+  if (tile == kPrefillTileRows / 2) return launch_t<D, kPrefillTileRows / 64, 2>(a, stream);
+  return launch_t<D, kPrefillTileRows / 128, 2>(a, stream);
 }
 
 }  // namespace

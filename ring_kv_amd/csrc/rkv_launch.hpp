@@ -44,12 +44,16 @@ constexpr int kVerifyFillWorkgroups = 256;
 constexpr int kPrefillTileRows = 256;
 // Row tile of the prefill kernel: kPrefillTileRows, or half of it (two waves per row group, one
 // per half of each chunk's keys) when the full tiles would leave most of the chip without a
-// workgroup (fewer than kPrefillFillWorkgroups).
+// workgroup (fewer than kPrefillFillWorkgroups), or a quarter of it (two row groups) where even
+// that grid of quarter tiles fits one round of kPrefillFillWorkgroups (a block over the ring).
 constexpr int kPrefillFillWorkgroups = 256;
 inline int prefill_tile_rows(int rows, int n_kv_heads, int num_splits) {
-  const int64_t full = (int64_t)n_kv_heads * num_splits *
-                       ((rows + kPrefillTileRows - 1) / kPrefillTileRows);
-  return full >= kPrefillFillWorkgroups ? kPrefillTileRows : kPrefillTileRows / 2;
+  auto grid = [&](int tile) {
+    return (int64_t)n_kv_heads * num_splits * ((rows + tile - 1) / tile);
+  };
+  if (grid(kPrefillTileRows) >= kPrefillFillWorkgroups) return kPrefillTileRows;
+  if (grid(kPrefillTileRows / 4) <= kPrefillFillWorkgroups) return kPrefillTileRows / 4;
+  return kPrefillTileRows / 2;
 }
 hipError_t launch_chunk_attn(const ChunkAttnArgs& a, hipStream_t stream);
 hipError_t launch_prefill_attn(const ChunkAttnArgs& a, hipStream_t stream);

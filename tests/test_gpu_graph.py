@@ -83,7 +83,7 @@ def test_graph_replay_matches_eager():
 
 def test_graph_replay_prefill_resident_and_paging():
     """The other entry points in a HIP graph: a 1,024-token prefill block over the pool (matrix-
-    core kernel, 4 splits, row-parallel merge) and over the ring (128-row tiles), attention over a
+    core kernel, 4 splits, row-parallel merge) and over the ring (64-row tiles), attention over a
     resident subset, and a page-out to pinned host memory followed by a page-in of long runs
     (copy engines) and of scattered ids (direct kernel).  Every replay reproduces the eager
     results bit for bit, with the outputs, the host store and the target pool clobbered by eager

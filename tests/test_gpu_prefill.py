@@ -20,8 +20,10 @@ pytestmark = pytest.mark.gpu
 # ---- the named prefill workloads -------------------------------------------------------------
 
 def test_prefill_pool_8k_splits_and_determinism():
-    """Splits 1 and 3 leave 256-row tiles short of the chip, so they run 128-row tiles (two waves
-    per row group, one per half of each chunk's keys); 0 (auto, 4) and 7 run 256-row tiles."""
+    """Splits 1 and 3 leave 256-row tiles short of the chip: 1 runs 64-row tiles (two row groups,
+    two waves per row group, one per half of each chunk's keys; that grid of 256 workgroups still
+    fits one round) and 3 runs 128-row tiles (its 64-row grid would take more than one round);
+    0 (auto, 4) and 7 run 256-row tiles."""
     c, _ = workload("prefill_pool_8k")
     say("prefill_pool_8k: oracle")
     ref = run_oracle(c)
