@@ -69,8 +69,9 @@ extern "C" {
 /* Rows per KV head, q_len * (n_q_heads / n_kv_heads), that one call may carry.  A verify block
  * (16 drafts: 64 rows at G = 4) and a batched prefill block (lucebox post, "TL;DR": prefill
  * as pooled batches plus ring attention; 1024 tokens: 4096 rows at G = 4) go through the same
- * calls.  Up to 256 rows the chunked calls stream the KV with 64-row tiles; longer blocks run a
- * matrix-core kernel with 64-, 128- or 256-row tiles.  Same definition, layouts and results. */
+ * calls.  Up to 256 rows the chunked calls stream the KV with 16-, 32- or 64-row tiles; longer
+ * blocks run a matrix-core kernel with 64-, 128- or 256-row tiles.  Same definition, layouts and
+ * results. */
 #define RKV_MAX_ROWS 16384
 
 typedef enum rkv_status {
