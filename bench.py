@@ -201,7 +201,7 @@ def attn_flops(c):
 class ReadProbe:
     """The streaming read probe (ring_kv_amd/libring_kv_probe.so): plain 16-byte loads over a
     buffer, nothing else.  Used to flush the caches without leaving dirty lines behind, and to
-    measure the HBM read bandwidth this machine delivers."""
+    measure the HBM read bandwidth this GPU delivers."""
 
     def __init__(self, torch):
         import ctypes
@@ -517,7 +517,7 @@ def paging_timings(torch, rk, reps):
 
 
 def read_bw_probe(torch, probe):
-    """Measured HBM read bandwidth on this machine: the streaming read probe over four 1 GiB buffers
+    """Measured HBM read bandwidth of this GPU: the streaming read probe over four 1 GiB buffers
     in turn (so no pass is served from the last-level cache), best of several grid sizes."""
     bufs = [torch.zeros(1 << 30, dtype=torch.uint8, device="cuda") for _ in range(4)]
     res = {}

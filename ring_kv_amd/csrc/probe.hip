@@ -1,7 +1,7 @@
 // Streaming HBM read probe, for measurement only (not part of the verify path): every
 // workgroup reads a contiguous share of a buffer with 16-byte non-temporal loads, eight per
 // thread in flight, and folds them into one word per thread so that no load is dead.  The
-// bench divides the bytes read by the time to report the bandwidth this machine delivers to a plain
+// bench divides the bytes read by the time to report the bandwidth this GPU delivers to a plain
 // read, next to the 8 TB/s specification.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
