@@ -155,7 +155,9 @@ int32_t verify_attn_ring(const rkv_attn_dims* dims, const void* q, const void* k
  * The key range is split into num_splits ranges of whole chunks (0: chosen from the
  * context and the chip's 256 compute units); each range yields a partial result
  * and a log-sum-exp merge combines them.  Any split gives the same result up to
- * f32 rounding.  One split spans at most 2^22 chunks (RKV_ERR_SHAPE otherwise):
+ * rounding: the bf16 weights of the PV product are rounded against each range's own
+ * running maximum, so split counts differ by about 1e-4 on N(0,1) inputs (within the
+ * bf16 tolerance of the exact result either way).  One split spans at most 2^22 chunks (RKV_ERR_SHAPE otherwise):
  * with num_splits = 1 that bounds ctx_len by 2^28.
  * ------------------------------------------------------------------------------- */
 size_t verify_attn_paged_workspace_bytes(const rkv_attn_dims* dims, int64_t ctx_len,

@@ -309,3 +309,21 @@ def test_layout_helpers_bit_exact():
     torch.cuda.synchronize()
     np.testing.assert_array_equal(kr.view(torch.int16).cpu().numpy().view(np.uint16), wk)
     np.testing.assert_array_equal(vr.view(torch.int16).cpu().numpy().view(np.uint16), wv)
+
+
+def test_each_verify_row_tile():
+    """The verify launch picks the smallest row tile whose grid fits one round of 256 workgroups:
+    at 8,192 positions, 8 splits run 16-row tiles (4 heads x 8 splits x 4 tiles = 128
+    workgroups), the automatic 32 splits 32-row tiles (256), and 64 splits 64-row tiles (256).
+    Each matches the oracle.  They differ from one another only by the rounding of the bf16
+    weights, which each key range takes against its own running maximum (~1e-4 here)."""
+    c = paged_case(911, 0, 8192, 16, 16, 4, 128)
+    ref = run_oracle(c)
+    outs = {}
+    for s in (8, 0, 64):
+        say(f"paged 8192 splits={s} (row tile by split count)")
+        outs[s] = run_gpu(c, num_splits=s)
+        assert_attn_close(outs[s], ref, "bf16", f"row tile S={s}")
+    for s in (8, 64):
+        assert np.abs(outs[s][0] - outs[0][0]).max() < 1e-3
+        assert np.abs(outs[s][1] - outs[0][1]).max() < 1e-4
