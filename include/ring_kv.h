@@ -6,11 +6,11 @@
  * at 256K context"):
  *   - a drafter proposes a block of tokens that the target checks in one batched
  *     forward ("The model, fast MoE with a drafter in the box");
- *   - sliding-window layers attend a position ring, slot = pos mod 2048, window 512
+ *   - sliding-window layers attend a ring indexed by position, slot = pos mod 2048, window 512
  *     ("3. Ring caches for the sliding-window layers");
  *   - full-attention layers attend a GPU pool of 64-token chunks ("Three
  *     optimizations", item 1, KVFlash paging), found through a page table;
- *   - only tokens the target itself would emit are committed: the longest agreeing
+ *   - what is committed equals what greedy decoding by the target produces: the longest agreeing
  *     drafted prefix plus the target's next token ("TL;DR"; "The model, fast MoE with
  *     a drafter in the box").
  *
@@ -25,8 +25,12 @@
  *   until the stream has passed the work.
  * Errors.  Every call returns an rkv_status.  All shape, dtype, pointer and size
  *   checks run on the host before any HIP call, so a rejected call touches no
- *   device state.  A failed launch returns RKV_ERR_HIP.  No C++ exception crosses
- *   this interface.
+ *   device state.  A failed launch returns RKV_ERR_HIP; the launch status is the
+ *   launch's own, so an error some earlier HIP call left in the thread's last-error
+ *   state is neither reported nor cleared.  No C++ exception crosses this interface.
+ * Device.  Split counts and row tiles follow the current device's compute-unit count
+ *   (queried once per device); the workspace sizes depend on it, so size and call on
+ *   the same device.
  * Determinism.  Identical inputs give bit-identical outputs: no float atomics, a
  *   fixed reduction order, and paged work ordered by logical chunk (never by
  *   physical slot), so permuting the pool changes nothing.
@@ -103,11 +107,19 @@ const char* rkv_status_str(int32_t status);
 
 /* ---------------------------------------------------------------------------------
  * Contiguous reference layout (GPU-side reference for the chunked calls, and plain
- * decode with q_len = 1).  Keys are positions 0 .. ctx_len-1 in k, v
- * [ctx_len][Hkv][D]; query i sits at ctx_len - q_len + i.  window = 0: full causal,
- * window > 0: sliding window of that many keys.  dtype f32 or bf16; every
- * arithmetic step runs in f32.  num_splits = 0 picks a split of the key range;
- * any value gives the same result up to f32 rounding.
+ * decode with q_len = 1).  The post verifies the whole drafted block in one batched
+ * forward whose result must equal decoding the tokens one at a time (lucebox post, "The
+ * model, fast MoE with a drafter in the box"); this call computes that batched attention
+ * over rows stored in plain position order, so row i of a block equals the q_len = 1
+ * call at context ctx_len - q_len + i + 1.  Keys are positions 0 .. ctx_len-1 in k, v
+ * [ctx_len][Hkv][D] (row-major, caller-owned device memory); query i sits at
+ * ctx_len - q_len + i.  window = 0: full causal, window > 0: sliding window of that
+ * many keys (the window layers' 512, "3. Ring caches for the sliding-window layers").
+ * dtype f32 or bf16; every arithmetic step runs in f32.  num_splits = 0 picks a split
+ * of the key range; any value gives the same result up to f32 rounding.  Workspace:
+ * decode_attn_ref_layout_workspace_bytes() bytes (0: none needed, NULL allowed).
+ * Status: RKV_ERR_NULL (q, k, v, out), RKV_ERR_SHAPE (dims, ctx_len < q_len),
+ * RKV_ERR_ARG (window or num_splits < 0), RKV_ERR_WORKSPACE, RKV_ERR_HIP.
  * ------------------------------------------------------------------------------- */
 size_t decode_attn_ref_layout_workspace_bytes(const rkv_attn_dims* dims, int64_t ctx_len,
                                               int32_t num_splits);
@@ -118,8 +130,8 @@ int32_t decode_attn_ref_layout(const rkv_attn_dims* dims, const void* q, const v
 
 /* ---------------------------------------------------------------------------------
  * Sliding-window verify attention over a position ring (lucebox post, "3. Ring caches
- * for the sliding-window layers": window layers keep a ring, slot = pos mod 2048, and
- * skip the pager).
+ * for the sliding-window layers": the window layers read a ring of their own, slot = pos
+ * mod 2048, instead of the paged pool).
  *   pos0       absolute position of query 0; query i sits at pos0 + i
  *   ring_head  the slot of query 0; must equal pos0 mod ring_size (checked)
  *   ring_size  positions the ring holds, a multiple of 64, >= window + q_len - 1
@@ -153,7 +165,7 @@ int32_t verify_attn_ring(const rkv_attn_dims* dims, const void* q, const void* k
  * contributes nothing (a contract breach, not an error the call can report).
  *
  * The key range is split into num_splits ranges of whole chunks (0: chosen from the
- * context and the chip's 256 compute units); each range yields a partial result
+ * context and the device's compute units, 256 on MI355X); each range yields a partial result
  * and a log-sum-exp merge combines them.  Any split gives the same result up to
  * rounding: the bf16 weights of the PV product are rounded against each range's own
  * running maximum, so split counts differ by about 1e-4 on N(0,1) inputs (within the
@@ -219,11 +231,15 @@ int32_t verify_accept(const float* logits, int32_t n_draft, int32_t vocab,
 
 /* ---------------------------------------------------------------------------------
  * Layout helpers: copy n contiguous rows k_src, v_src [n][Hkv][D] holding positions
- * pos_first .. pos_first+n-1 into a ring (slot = pos mod ring_size) or into the
- * paged pool (slot page_table[pos/64], offset pos mod 64), K key-major and V
- * dimension-major per chunk.  This is also how a verify block's own rows are
- * appended before attention.  dtype must be bf16.  For the ring, n <= ring_size.
- * Pool entries outside [0, n_slots) are skipped on the device.
+ * pos_first .. pos_first+n-1 into a ring or into the paged pool, K key-major and V
+ * dimension-major per chunk.  The ring puts position p at slot p mod ring_size (lucebox
+ * post, "3. Ring caches for the sliding-window layers": slot = pos mod 2048); the pool
+ * puts it in chunk p / 64 at offset p mod 64, the chunk living in slot page_table[p/64]
+ * ("Three optimizations", item 1: 64-token chunks).  This is also how a verify block's
+ * own rows are appended before attention.  All pointers are caller-owned device memory;
+ * dtype must be bf16.  For the ring, n <= ring_size (RKV_ERR_RING otherwise); for the
+ * pool, the table must cover the last position (RKV_ERR_TABLE).  Pool entries outside
+ * [0, n_slots) are skipped on the device.  n = 0 does nothing.
  * ------------------------------------------------------------------------------- */
 int32_t ref_layout_to_ring(const void* k_src, const void* v_src, int64_t pos_first, int64_t n,
                            int32_t n_kv_heads, int32_t head_dim, int32_t dtype, void* k_ring,
@@ -239,8 +255,8 @@ int32_t ref_layout_to_paged(const void* k_src, const void* v_src, int64_t pos_fi
  * n K/V rows (positions ctx .. ctx+n-1) join the stores; after the accept, the a+1 kept
  * rows are committed and the rest are left to be overwritten (lucebox post, "3. Ring
  * caches for the sliding-window layers": slot = pos mod 2048; "Three optimizations",
- * item 1: a pool of 64-token chunks located through a page table; the verify step
- * commits only the tokens the target itself would emit).
+ * item 1: a pool of 64-token chunks located through a page table; the verify step keeps
+ * exactly what greedy decoding by the target would produce).
  *
  * Ring: verify_kv_append_ring writes row i (position pos_first+i) at ring slot
  * (pos_first+i) mod ring_size, 1 <= n <= RKV_MAX_APPEND, n <= ring_size.  Rolling back
@@ -297,9 +313,58 @@ int32_t verify_kv_append_paged(const void* k_new, const void* v_new, int32_t n,
                                int32_t n_new, const int32_t* new_slots, void* stream);
 
 /* ---------------------------------------------------------------------------------
- * Host paging of the pool (lucebox post, "Three optimizations", item 1: the pool keeps part of
- * the context on the GPU and cold 64-token chunks page to host RAM bit-exact; which chunks
- * stay resident is scored by the drafter, outside this library).
+ * One captured step replayed across decode steps (lucebox post, "The model, fast MoE with a
+ * drafter in the box": the decode loop is fused and replayed as a graph; "Three
+ * optimizations", item 1: prefill blocks are graph replays too).  A captured HIP graph
+ * replays the kernel arguments it recorded, so a step whose positions are arguments can
+ * only be replayed at the same positions.  These calls read the block's position from
+ * device memory instead:
+ *   d_pos   device int64: the absolute position of the block's first row, which is the
+ *           committed length of the sequence (query i and appended row i sit at *d_pos + i;
+ *           the pool's context is *d_pos + q_len)
+ *   pos_cap the largest value *d_pos may take while the graph is replayed; the split layout
+ *           (and the workspace) cover every position up to it
+ * and verify_pos_advance moves *d_pos past the tokens a step committed, on the device:
+ *   *d_pos += *accept_len + 1     (the a accepted drafts and the target's next token)
+ * so that append -> attention -> accept -> advance, captured once, is the decode loop.
+ * The pool calls read the slot of every chunk from page_table: the caller reserves the
+ * slots of every chunk the positions up to pos_cap + n can reach before capturing (there
+ * is no allocation inside a replay).  A device value outside [0, pos_cap] makes the
+ * attention calls write NaN to out and lse and the append calls write nothing.  Same
+ * definition, layouts and results as verify_attn_ring / verify_attn_paged /
+ * verify_kv_append_* at the position *d_pos holds when the stream runs the call; verify
+ * blocks only (q_len * G <= 256, RKV_ERR_SHAPE otherwise).
+ *   ring workspace: verify_attn_ring_workspace_bytes(dims, ring_size, window, num_splits)
+ *   pool workspace: verify_attn_paged_workspace_bytes(dims, pos_cap + q_len, 64, num_splits)
+ * Status as the position-argument calls, plus RKV_ERR_NULL for d_pos and RKV_ERR_ARG for
+ * pos_cap < 0; the pool calls return RKV_ERR_TABLE when the table cannot hold position
+ * pos_cap + q_len - 1 (attention) or pos_cap + n - 1 (append).
+ * ------------------------------------------------------------------------------- */
+int32_t verify_attn_ring_dev(const rkv_attn_dims* dims, const void* q, const void* k_ring,
+                             const void* v_ring, const int64_t* d_pos, int64_t pos_cap,
+                             int32_t ring_size, int32_t window, int32_t num_splits,
+                             void* workspace, size_t workspace_bytes, float* out, float* lse,
+                             void* stream);
+int32_t verify_attn_paged_dev(const rkv_attn_dims* dims, const void* q, const void* k_pool,
+                              const void* v_pool, const int32_t* page_table, int32_t n_table,
+                              int32_t n_slots, int32_t chunk_size, const int64_t* d_pos,
+                              int64_t pos_cap, int32_t num_splits, void* workspace,
+                              size_t workspace_bytes, float* out, float* lse, void* stream);
+int32_t verify_kv_append_ring_dev(const void* k_new, const void* v_new, int32_t n,
+                                  const int64_t* d_pos, int64_t pos_cap, int32_t n_kv_heads,
+                                  int32_t head_dim, void* k_ring, void* v_ring, int32_t ring_size,
+                                  void* stream);
+int32_t verify_kv_append_paged_dev(const void* k_new, const void* v_new, int32_t n,
+                                   const int64_t* d_pos, int64_t pos_cap, int32_t n_kv_heads,
+                                   int32_t head_dim, void* k_pool, void* v_pool,
+                                   const int32_t* page_table, int32_t n_table, int32_t n_slots,
+                                   void* stream);
+int32_t verify_pos_advance(int64_t* d_pos, const int32_t* accept_len, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Host paging of the pool (lucebox post, "Three optimizations", item 1: only part of the
+ * context stays in the GPU pool and 64-token chunks move to host memory and back without any
+ * change to their bits; the drafter scores which chunks stay, outside this library).
  *
  * Host chunk store: k_host [n_host][Hkv][64][D], v_host [n_host][Hkv][D][64] bf16 in host
  * memory, one entry per logical chunk (entry c holds chunk c), laid out like a pool slot.

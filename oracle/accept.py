@@ -14,8 +14,8 @@ If row r is the target's distribution given the committed prefix and prop[0..r),
 then committed equals a+1 steps of plain greedy decoding, so the output is exactly
 the target's own (lucebox post "Laguna XS 2.1 33B on a RTX 3090: 296 tok/s peak,
 152 tok/s at 256K context", "The model, fast MoE with a drafter in the box": the
-proposals are verified in one batched forward and only tokens the target itself
-would emit are committed; "TL;DR": the decode is verify-exact).
+proposals are verified in one batched forward and what is kept equals greedy decoding
+by the target; "TL;DR": the decode is verify-exact).
 
 The argmax compares float32 values as float32 (the logits' own precision); -0.0 and
 +0.0 compare equal, so the lower index wins.  Inputs must be finite.

@@ -6,9 +6,9 @@ context"):
 
 * The verify block is one batched forward over the drafted tokens ("The model, fast MoE with a
   drafter in the box"), so its own K/V rows (positions ctx .. ctx+n-1) are in the stores when
-  its attention runs, and only the tokens the target itself would emit are committed (same
-  section, "commits only tokens the target itself would emit").
-* Window layers keep a position ring, slot = pos mod 2048 ("3. Ring caches for the
+  its attention runs, and the tokens it keeps are exactly those plain greedy decoding by the
+  target would have produced (same section: the verification is greedy-exact).
+* Window layers keep a ring indexed by position, slot = pos mod 2048 ("3. Ring caches for the
   sliding-window layers"): row of position p is written at ring slot p mod R.
 * Full-attention layers keep a pool of 64-token chunks located through a page table ("Three
   optimizations", item 1): position p lives in slot table[p // 64] at offset p % 64.
@@ -21,9 +21,9 @@ back.  Which free slot is handed out is a policy, not part of the method; ``Page
 states the one the library uses (a stack that starts as 0, 1, 2, ...; a block's unused
 chunks are returned last chunk first, so the earliest is handed out first again).
 
-Host paging (same post, "Three optimizations", item 1: the pool keeps part of the context on the
-GPU, cold 64-token chunks page to host RAM bit-exact, and which chunks stay is a scoring
-question outside this path).  A host chunk store holds one entry per logical chunk, laid out like
+Host paging (same post, "Three optimizations", item 1: only part of the context stays in the
+GPU pool, 64-token chunks that are not needed move to host memory without any change to their
+bits, and which chunks stay is a scoring question outside this path).  A host chunk store holds one entry per logical chunk, laid out like
 a pool slot; paging a chunk out copies its slot to the chunk's host entry and frees the slot,
 paging it in copies the entry into a free slot.  Attention of a block over the resident subset
 attends exactly the keys of the chunks that have a slot, at their own positions.
@@ -75,7 +75,7 @@ def append_paged(k_pool, v_pool, table, k_new, v_new, pos_first: int):
 
 def page_out(k_pool, v_pool, slots, chunk_ids, k_host, v_host):
     """Host entries chunk_ids[i] <- pool slot slots[i] (K and V), bit for bit (lucebox post,
-    "Three optimizations", item 1: cold chunks page to host RAM).  Returns the new host stores."""
+    "Three optimizations", item 1: chunks move between the pool and host memory).  Returns the new host stores."""
     kh = np.array(k_host, copy=True)
     vh = np.array(v_host, copy=True)
     for s, c in zip(slots, chunk_ids):

@@ -70,6 +70,15 @@ _PROTOS = {
                              _P, c_size_t, _P]),
     "verify_attn_paged_resident": (c_int32, [_DIMS, _P, _P, _P, _P, _P, c_int32, c_int32, c_int64,
                                              c_int32, _P, c_size_t, _P, _P, _P]),
+    "verify_attn_ring_dev": (c_int32, [_DIMS, _P, _P, _P, _P, c_int64, c_int32, c_int32, c_int32,
+                                       _P, c_size_t, _P, _P, _P]),
+    "verify_attn_paged_dev": (c_int32, [_DIMS, _P, _P, _P, _P, c_int32, c_int32, c_int32, _P,
+                                        c_int64, c_int32, _P, c_size_t, _P, _P, _P]),
+    "verify_kv_append_ring_dev": (c_int32, [_P, _P, c_int32, _P, c_int64, c_int32, c_int32, _P,
+                                            _P, c_int32, _P]),
+    "verify_kv_append_paged_dev": (c_int32, [_P, _P, c_int32, _P, c_int64, c_int32, c_int32, _P,
+                                             _P, _P, c_int32, c_int32, _P]),
+    "verify_pos_advance": (c_int32, [_P, _P, _P]),
     "rkv_pager_evict": (c_int32, [c_void_p, _P, c_int32, _P]),
     "rkv_pager_restore": (c_int32, [c_void_p, _P, c_int32, _P]),
     "rkv_pager_resident": (c_int32, [c_void_p, _P, _P, c_int32]),

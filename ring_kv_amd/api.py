@@ -452,6 +452,96 @@ def verify_attn_paged_resident(q, k_pool, v_pool, d_slots, chunk_ids, ctx_len: i
     return out, lse
 
 
+def _pos_tensor(d_pos, device):
+    """The device-resident block position: one int64 on the calls' device."""
+    _form(d_pos, "d_pos", torch.int64, (1,))
+    _on(device, d_pos=d_pos)
+
+
+def verify_attn_ring_dev(q, k_ring, v_ring, d_pos, pos_cap: int, window: int, *,
+                         num_splits: int = 0, scale: float = 0.0, out=None, lse=None,
+                         want_lse: bool = True, workspace=None, stream=None):
+    """verify_attn_ring with the block's first position read from d_pos (int64 [1], device)
+    when the stream runs the call: a captured graph replays at whatever *d_pos holds."""
+    _form(q, "q", torch.bfloat16, (None, None, None))
+    q_len, hq, d = q.shape
+    n_chunks, hkv, _ = _chunked(k_ring, v_ring, "k_ring", "v_ring", d)
+    dev = q.device
+    _pos_tensor(d_pos, dev)
+    out, lse = _outputs(q_len, hq, d, dev, out, lse, want_lse)
+    _on(dev, q=q, k_ring=k_ring, v_ring=v_ring)
+    ring_size = n_chunks * CHUNK
+    dims = _dims(q, hkv, scale)
+    L = lib()
+    ws, wsb = _workspace(L.verify_attn_ring_workspace_bytes(ctypes.byref(dims), ring_size, window,
+                                                            num_splits), dev, workspace)
+    check("verify_attn_ring_dev", L.verify_attn_ring_dev(
+        ctypes.byref(dims), _ptr(q), _ptr(k_ring), _ptr(v_ring), _ptr(d_pos), pos_cap, ring_size,
+        window, num_splits, _ptr(ws), wsb, _ptr(out), _ptr(lse), _stream(stream, dev)))
+    return out, lse
+
+
+def verify_attn_paged_dev(q, k_pool, v_pool, page_table, d_pos, pos_cap: int, *,
+                          num_splits: int = 0, scale: float = 0.0, out=None, lse=None,
+                          want_lse: bool = True, workspace=None, stream=None):
+    """verify_attn_paged at context *d_pos + q_len, read from the device when the stream runs
+    the call; splits and workspace cover every position up to pos_cap."""
+    _form(q, "q", torch.bfloat16, (None, None, None))
+    q_len, hq, d = q.shape
+    n_slots, hkv, _ = _chunked(k_pool, v_pool, "k_pool", "v_pool", d)
+    _form(page_table, "page_table", torch.int32, (None,))
+    dev = q.device
+    _pos_tensor(d_pos, dev)
+    out, lse = _outputs(q_len, hq, d, dev, out, lse, want_lse)
+    _on(dev, q=q, k_pool=k_pool, v_pool=v_pool, page_table=page_table)
+    dims = _dims(q, hkv, scale)
+    L = lib()
+    ws, wsb = _workspace(L.verify_attn_paged_workspace_bytes(ctypes.byref(dims), pos_cap + q_len,
+                                                             CHUNK, num_splits), dev, workspace)
+    check("verify_attn_paged_dev", L.verify_attn_paged_dev(
+        ctypes.byref(dims), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
+        page_table.numel(), n_slots, CHUNK, _ptr(d_pos), pos_cap, num_splits, _ptr(ws), wsb,
+        _ptr(out), _ptr(lse), _stream(stream, dev)))
+    return out, lse
+
+
+def verify_kv_append_ring_dev(k_new, v_new, d_pos, pos_cap: int, k_ring, v_ring, *, stream=None):
+    """Append rows k_new, v_new [n][Hkv][D] at positions *d_pos .. (device-resident) to the ring."""
+    n, hkv, d = _rows_pair(k_new, v_new, "k_new", "v_new")
+    n_chunks, _, _ = _chunked(k_ring, v_ring, "k_ring", "v_ring", d, hkv)
+    dev = k_new.device
+    _pos_tensor(d_pos, dev)
+    _on(dev, k_new=k_new, v_new=v_new, k_ring=k_ring, v_ring=v_ring)
+    check("verify_kv_append_ring_dev", lib().verify_kv_append_ring_dev(
+        _ptr(k_new), _ptr(v_new), n, _ptr(d_pos), pos_cap, hkv, d, _ptr(k_ring), _ptr(v_ring),
+        n_chunks * CHUNK, _stream(stream, dev)))
+
+
+def verify_kv_append_paged_dev(k_new, v_new, d_pos, pos_cap: int, k_pool, v_pool, page_table, *,
+                               stream=None):
+    """Append rows at positions *d_pos .. to the pool, each chunk's slot read from page_table
+    (reserved by the caller for every chunk up to position pos_cap + n - 1)."""
+    n, hkv, d = _rows_pair(k_new, v_new, "k_new", "v_new")
+    n_slots, _, _ = _chunked(k_pool, v_pool, "k_pool", "v_pool", d, hkv)
+    _form(page_table, "page_table", torch.int32, (None,))
+    dev = k_new.device
+    _pos_tensor(d_pos, dev)
+    _on(dev, k_new=k_new, v_new=v_new, k_pool=k_pool, v_pool=v_pool, page_table=page_table)
+    check("verify_kv_append_paged_dev", lib().verify_kv_append_paged_dev(
+        _ptr(k_new), _ptr(v_new), n, _ptr(d_pos), pos_cap, hkv, d, _ptr(k_pool), _ptr(v_pool),
+        _ptr(page_table), page_table.numel(), n_slots, _stream(stream, dev)))
+
+
+def verify_pos_advance(d_pos, accept_len, *, stream=None):
+    """*d_pos += *accept_len + 1 on the device (the tokens one decode step committed)."""
+    dev = d_pos.device
+    _pos_tensor(d_pos, dev)
+    _form(accept_len, "accept_len", torch.int32, (1,))
+    _on(dev, accept_len=accept_len)
+    check("verify_pos_advance", lib().verify_pos_advance(_ptr(d_pos), _ptr(accept_len),
+                                                         _stream(stream, dev)))
+
+
 def tensor_from_numpy(arr, device="cuda", bf16_bits: Optional[bool] = None) -> torch.Tensor:
     """Copy a numpy array to the device; uint16 arrays are bf16 bit patterns."""
     import numpy as np

@@ -3,16 +3,38 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/ring_kv.h"
 #include "rkv_launch.hpp"
+
+namespace rkv {
+
+// The verify kernels run one workgroup per compute unit (each takes a unit's LDS or registers),
+// so split counts and row tiles are chosen from the device's unit count: 256 on a whole MI355X,
+// fewer on a partitioned one.  Cached per device; the fallback is a whole MI355X.
+int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  constexpr int kDefault = 256;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return kDefault;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    n = kDefault;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+}  // namespace rkv
 
 namespace {
 
 using rkv::ChunkAttnArgs;
 
 constexpr int kChunk = RKV_CHUNK;
-// MI355X has 256 compute units; the verify kernels run one 128-KiB-LDS workgroup per unit.
-constexpr int kTargetWorkgroups = 256;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -46,7 +68,7 @@ int64_t auto_split_target(const rkv_attn_dims* d, Store store) {
   if (prefill && store == kRing) return 1;
   const int tile = prefill ? rkv::kPrefillTileRows : 64;
   const int64_t units = (int64_t)d->n_kv_heads * ((rows + tile - 1) / tile);
-  return (kTargetWorkgroups + units - 1) / units;
+  return (rkv::device_cu_count() + units - 1) / units;
 }
 
 // The paged store's automatic split target for a context of n_chunks chunks.  A verify block's
@@ -118,6 +140,7 @@ int32_t run_chunk_attn(ChunkAttnArgs& a, const rkv_attn_dims* d, void* ws, float
   a.out = out;
   a.lse = lse;
   a.part_o = a.part_lse = nullptr;
+  a.fill_wgs = rkv::device_cu_count();
   if (a.num_splits > 1) carve(ws, d, a.num_splits, &a.part_o, &a.part_lse);
   hipError_t e = rkv::launch_chunk_attn(a, st);
   if (e != hipSuccess || a.num_splits == 1) return hip_status(e);
@@ -410,7 +433,74 @@ int32_t verify_attn_paged_partial(const rkv_attn_dims* dims, const void* q,
   if (a.cps > rkv::kMaxSplitChunks) return RKV_ERR_SHAPE;
   a.part_o = part_out;     // partial layout even for one split
   a.part_lse = part_lse;
+  a.fill_wgs = rkv::device_cu_count();
   return hip_status(rkv::launch_chunk_attn(a, static_cast<hipStream_t>(stream)));
+}
+
+// ---- one captured step replayed across decode steps: the block position on the device ----
+
+int32_t verify_attn_ring_dev(const rkv_attn_dims* dims, const void* q, const void* k_ring,
+                             const void* v_ring, const int64_t* d_pos, int64_t pos_cap,
+                             int32_t ring_size, int32_t window, int32_t num_splits,
+                             void* workspace, size_t workspace_bytes, float* out, float* lse,
+                             void* stream) {
+  int32_t st = check_ring(dims, q, k_ring, v_ring, 0, 0, ring_size, window);
+  if (st != RKV_OK) return st;
+  if (d_pos == nullptr || out == nullptr) return RKV_ERR_NULL;
+  if (rows_of(dims) > rkv::kVerifyMaxRows) return RKV_ERR_SHAPE;
+  if (pos_cap < 0 || num_splits < 0) return RKV_ERR_ARG;
+  // the split layout covers the widest span any position can have
+  const int64_t n_max = ring_max_chunks(dims, window);
+  int32_t s, cps;
+  choose_splits(n_max, auto_split_target(dims, kRing), num_splits, &s, &cps);
+  if (s > 1 && (workspace == nullptr || workspace_bytes < partial_bytes(dims, s)))
+    return RKV_ERR_WORKSPACE;
+  ChunkAttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k_ring);
+  a.v = static_cast<const uint16_t*>(v_ring);
+  a.pt = nullptr;
+  a.n_slots = ring_size / kChunk;
+  a.q_len = dims->q_len;
+  a.G = dims->n_q_heads / dims->n_kv_heads;
+  a.n_q_heads = dims->n_q_heads;
+  a.n_kv_heads = dims->n_kv_heads;
+  a.head_dim = dims->head_dim;
+  a.window = window;
+  a.n_chunks = n_max;
+  a.cps = cps;
+  a.num_splits = s;
+  a.scale_log2 = scale_log2(dims);
+  a.d_pos = d_pos;
+  a.pos_cap = pos_cap;
+  a.ring_size = ring_size;
+  return run_chunk_attn(a, dims, workspace, out, lse, static_cast<hipStream_t>(stream));
+}
+
+int32_t verify_attn_paged_dev(const rkv_attn_dims* dims, const void* q, const void* k_pool,
+                              const void* v_pool, const int32_t* page_table, int32_t n_table,
+                              int32_t n_slots, int32_t chunk_size, const int64_t* d_pos,
+                              int64_t pos_cap, int32_t num_splits, void* workspace,
+                              size_t workspace_bytes, float* out, float* lse, void* stream) {
+  if (dims == nullptr) return RKV_ERR_NULL;
+  if (pos_cap < 0 || pos_cap > INT64_MAX / 2) return RKV_ERR_ARG;
+  const int64_t ctx_max = pos_cap + dims->q_len;
+  int32_t st = check_paged(dims, q, k_pool, v_pool, page_table, n_table, n_slots, chunk_size,
+                           ctx_max);
+  if (st != RKV_OK) return st;
+  if (d_pos == nullptr || out == nullptr) return RKV_ERR_NULL;
+  if (rows_of(dims) > rkv::kVerifyMaxRows) return RKV_ERR_SHAPE;
+  if (num_splits < 0) return RKV_ERR_ARG;
+  // the split layout is that of the largest context the position can reach
+  ChunkAttnArgs a = paged_args(dims, q, k_pool, v_pool, page_table, n_slots, ctx_max);
+  choose_splits(a.n_chunks, paged_split_target(dims, a.n_chunks), num_splits, &a.num_splits,
+                &a.cps);
+  if (a.num_splits > 1 &&
+      (workspace == nullptr || workspace_bytes < partial_bytes(dims, a.num_splits)))
+    return RKV_ERR_WORKSPACE;
+  a.d_pos = d_pos;
+  a.pos_cap = pos_cap;
+  return run_chunk_attn(a, dims, workspace, out, lse, static_cast<hipStream_t>(stream));
 }
 
 int32_t attn_merge_partials(const rkv_attn_dims* dims, int32_t num_splits,
@@ -549,6 +639,65 @@ int32_t verify_kv_append_ring(const void* k_new, const void* v_new, int32_t n,
   a.n_slots = ring_size / kChunk;
   a.ring_size = ring_size;
   return hip_status(rkv::launch_scatter(a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t verify_kv_append_ring_dev(const void* k_new, const void* v_new, int32_t n,
+                                  const int64_t* d_pos, int64_t pos_cap, int32_t n_kv_heads,
+                                  int32_t head_dim, void* k_ring, void* v_ring, int32_t ring_size,
+                                  void* stream) {
+  if (k_new == nullptr || v_new == nullptr || k_ring == nullptr || v_ring == nullptr ||
+      d_pos == nullptr)
+    return RKV_ERR_NULL;
+  if (n_kv_heads < 1 || (head_dim != 64 && head_dim != 128)) return RKV_ERR_SHAPE;
+  if (n < 1 || n > RKV_MAX_APPEND || pos_cap < 0) return RKV_ERR_ARG;
+  if (ring_size < kChunk || ring_size % kChunk != 0 || n > ring_size) return RKV_ERR_RING;
+  rkv::ScatterArgs a{};
+  a.k_src = static_cast<const uint16_t*>(k_new);
+  a.v_src = static_cast<const uint16_t*>(v_new);
+  a.n = n;
+  a.n_kv_heads = n_kv_heads;
+  a.head_dim = head_dim;
+  a.k_dst = static_cast<uint16_t*>(k_ring);
+  a.v_dst = static_cast<uint16_t*>(v_ring);
+  a.n_slots = ring_size / kChunk;
+  a.ring_size = ring_size;
+  a.d_pos = d_pos;
+  a.pos_cap = pos_cap;
+  return hip_status(rkv::launch_scatter(a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t verify_kv_append_paged_dev(const void* k_new, const void* v_new, int32_t n,
+                                   const int64_t* d_pos, int64_t pos_cap, int32_t n_kv_heads,
+                                   int32_t head_dim, void* k_pool, void* v_pool,
+                                   const int32_t* page_table, int32_t n_table, int32_t n_slots,
+                                   void* stream) {
+  if (k_new == nullptr || v_new == nullptr || k_pool == nullptr || v_pool == nullptr ||
+      page_table == nullptr || d_pos == nullptr)
+    return RKV_ERR_NULL;
+  if (n_kv_heads < 1 || (head_dim != 64 && head_dim != 128)) return RKV_ERR_SHAPE;
+  if (n < 1 || n > RKV_MAX_APPEND || pos_cap < 0) return RKV_ERR_ARG;
+  if (n_slots < 1 || n_table < 1) return RKV_ERR_TABLE;
+  if ((pos_cap + n + kChunk - 1) / kChunk > n_table) return RKV_ERR_TABLE;
+  rkv::ScatterArgs a{};
+  a.k_src = static_cast<const uint16_t*>(k_new);
+  a.v_src = static_cast<const uint16_t*>(v_new);
+  a.n = n;
+  a.n_kv_heads = n_kv_heads;
+  a.head_dim = head_dim;
+  a.k_dst = static_cast<uint16_t*>(k_pool);
+  a.v_dst = static_cast<uint16_t*>(v_pool);
+  a.pt = page_table;
+  a.n_table = n_table;
+  a.n_slots = n_slots;
+  a.d_pos = d_pos;
+  a.pos_cap = pos_cap;
+  return hip_status(rkv::launch_scatter(a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t verify_pos_advance(int64_t* d_pos, const int32_t* accept_len, void* stream) {
+  if (d_pos == nullptr || accept_len == nullptr) return RKV_ERR_NULL;
+  rkv::AdvanceArgs a{d_pos, accept_len};
+  return hip_status(rkv::launch_advance(a, static_cast<hipStream_t>(stream)));
 }
 
 int32_t verify_kv_append_paged(const void* k_new, const void* v_new, int32_t n,

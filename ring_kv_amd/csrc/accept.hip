@@ -1,7 +1,7 @@
 // Greedy acceptance (lucebox post "Laguna XS 2.1 33B on a RTX 3090: 296 tok/s peak, 152 tok/s
 // at 256K context", "TL;DR" and "The model, fast MoE with a drafter in the box": proposals are
-// verified in one batched forward and only tokens the target itself would emit are
-// committed).  Pass 1: every workgroup finds the first maximum of one (row, vocabulary part),
+// verified in one batched forward and what is committed is what greedy decoding by the
+// target would produce).  Pass 1: every workgroup finds the first maximum of one (row, vocabulary part),
 // reduced within a wave by shuffles and across waves through LDS.  Pass 2 (one workgroup):
 // the parts reduce to the row argmaxes, then the first disagreement with the draft and the
 // committed tokens.  Ties go to the lower index, values compare as float32 (-0 == +0).
@@ -150,18 +150,25 @@ __global__ __launch_bounds__(256) void accept_final_kernel(AcceptArgs a) {
   if (tid < a.n_rows) a.committed[tid] = tid < acc ? prop[tid] : (tid == acc ? t[acc] : -1);
 }
 
+// The commit of one decode step on the device: the next block starts a + 1 positions later
+// (the a accepted drafts and the target's own next token).
+__global__ __launch_bounds__(64) void advance_kernel(AdvanceArgs a) {
+  if (threadIdx.x == 0) a.pos[0] += (int64_t)a.accept_len[0] + 1;
+}
+
 }  // namespace
 
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream) {
   const dim3 grid(a.parts, a.n_rows);
-  if ((a.vocab & 3) == 0 && (a.part_len & 3) == 0)
-    hipLaunchKernelGGL(accept_partial_kernel<true>, grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(accept_partial_kernel<false>, grid, dim3(256), 0, stream, a);
-  hipError_t e = hipGetLastError();
+  const hipError_t e = (a.vocab & 3) == 0 && (a.part_len & 3) == 0
+                           ? launch_kernel(accept_partial_kernel<true>, grid, dim3(256), a, stream)
+                           : launch_kernel(accept_partial_kernel<false>, grid, dim3(256), a, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(accept_final_kernel, dim3(1), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  return launch_kernel(accept_final_kernel, dim3(1), dim3(256), a, stream);
+}
+
+hipError_t launch_advance(const AdvanceArgs& a, hipStream_t stream) {
+  return launch_kernel(advance_kernel, dim3(1), dim3(64), a, stream);
 }
 
 }  // namespace rkv

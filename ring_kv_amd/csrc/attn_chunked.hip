@@ -138,8 +138,32 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
   const int G = a.G;
   const int rows = a.q_len * G;
 
-  const int64_t c_lo = a.c_first + (int64_t)s * a.cps;
-  const int64_t c_end = a.c_first + a.n_chunks;
+  // Positions of the block: from the arguments, or derived from the device-resident position
+  // of its first row (one captured step replayed as the context grows).  A pool split's first
+  // chunk does not depend on it (pool keys start at position 0), so the first table reads need
+  // not wait for it.
+  int64_t p0 = a.p0, valid_lo = a.valid_lo, valid_hi = a.valid_hi;
+  int64_t c_first = PAGED ? 0 : a.c_first, n_chunks = a.n_chunks;
+  bool pos_bad = false;
+  if (a.d_pos != nullptr) {
+    const int64_t P = *a.d_pos;
+    pos_bad = P < 0 || P > a.pos_cap;
+    p0 = pos_bad ? 0 : P;
+    const int64_t end = p0 + a.q_len;
+    valid_hi = end;
+    if (PAGED) {
+      valid_lo = 0;
+      n_chunks = (end + kChunk - 1) / kChunk;
+    } else {
+      const int64_t lo = a.window > 0 ? imax64(0, p0 - a.window + 1) : 0;
+      c_first = lo / kChunk;
+      n_chunks = (end - 1) / kChunk - c_first + 1;
+      valid_lo = imax64(0, end - a.ring_size);
+    }
+  }
+
+  const int64_t c_lo = c_first + (int64_t)s * a.cps;
+  const int64_t c_end = c_first + n_chunks;
   const int nloc = (int)imax64(0, imin64((int64_t)a.cps, c_end - c_lo));
 
   // ---- this lane's query row (row tile blockIdx.y holds rows 16*NRG*y ..) ----------------
@@ -151,14 +175,14 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
   const bool wave_active = row0 + rg * 16 < rows;
   // key position bounds, relative to this split's first key c_lo * 64
   const int64_t pbase = c_lo * 64;
-  const int64_t p_i64 = a.p0 + qi;
+  const int64_t p_i64 = p0 + qi;
   const int p_i = rel_pos(p_i64, pbase);                             // this row's query
   const int lo_i = rel_pos(a.window > 0 ? imax64(0, p_i64 - a.window + 1) : 0, pbase);
-  const int p_first = rel_pos(a.p0, pbase);                          // first query of the block
-  const int64_t p_last = a.p0 + a.q_len - 1;
+  const int p_first = rel_pos(p0, pbase);                            // first query of the block
+  const int64_t p_last = p0 + a.q_len - 1;
   const int lo_last = rel_pos(a.window > 0 ? imax64(0, p_last - a.window + 1) : 0, pbase);
-  const int vlo = rel_pos(a.valid_lo, pbase);                        // stored keys [vlo, vhi)
-  const int vhi = rel_pos(a.valid_hi, pbase);
+  const int vlo = rel_pos(valid_lo, pbase);                          // stored keys [vlo, vhi)
+  const int vhi = rel_pos(valid_hi, pbase);
 
   // Q^T operand of S^T = K Q^T: lane (ln, lq) holds row ln's dims kk*32 + 8*lq .. +7
   bf16x8 qop[KK];
@@ -585,8 +609,10 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
     }
   }
   if (!wave_active || !row_ok) return;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  const float lse_nat = lfr > 0.f ? (m_run + log2f(lfr)) * kLn2 : -INFINITY;
+  // a device position out of range: every output of the call is NaN
+  const float inv = pos_bad ? __builtin_nanf("") : (l > 0.f ? 1.f / l : 0.f);
+  const float lse_nat = pos_bad ? __builtin_nanf("")
+                                : (lfr > 0.f ? (m_run + log2f(lfr)) * kLn2 : -INFINITY);
   float* dst;
   if (a.part_o == nullptr) {
     dst = a.out + ((int64_t)qi * a.n_q_heads + hq) * D;
@@ -608,11 +634,8 @@ hipError_t launch_t(const ChunkAttnArgs& a, hipStream_t stream) {
   const int rows = a.q_len * a.G;
   const dim3 blocks(a.n_kv_heads * a.num_splits, (rows + NRG * 16 - 1) / (NRG * 16));
   const dim3 threads(NRG * KS * 64);
-  if (a.pt != nullptr)
-    hipLaunchKernelGGL((chunk_attn_kernel<D, NRG, KS, true>), blocks, threads, 0, stream, a);
-  else
-    hipLaunchKernelGGL((chunk_attn_kernel<D, NRG, KS, false>), blocks, threads, 0, stream, a);
-  return hipGetLastError();
+  if (a.pt != nullptr) return launch_kernel(chunk_attn_kernel<D, NRG, KS, true>, blocks, threads, a, stream);
+  return launch_kernel(chunk_attn_kernel<D, NRG, KS, false>, blocks, threads, a, stream);
 }
 
 // Tiles of 64 rows (blockIdx.y), two waves per row group (key halves).  Tiles of one split
@@ -628,8 +651,8 @@ template <int D>
 hipError_t launch_d(const ChunkAttnArgs& a, hipStream_t stream) {
   const int rows = a.q_len * a.G;
   const int64_t wgs = (int64_t)a.n_kv_heads * a.num_splits * ((rows + 63) / 64);
-  if (4 * wgs <= kVerifyFillWorkgroups) return launch_t<D, 1, 2>(a, stream);
-  if (2 * wgs <= kVerifyFillWorkgroups) return launch_t<D, 2, 2>(a, stream);
+  if (4 * wgs <= a.fill_wgs) return launch_t<D, 1, 2>(a, stream);
+  if (2 * wgs <= a.fill_wgs) return launch_t<D, 2, 2>(a, stream);
   return launch_t<D, 4, 2>(a, stream);
 }
 

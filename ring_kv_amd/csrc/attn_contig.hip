@@ -202,11 +202,8 @@ template <int D>
 hipError_t launch_d(const ContigArgs& a, hipStream_t stream) {
   const int rows = a.q_len * a.G;
   const dim3 grid(a.n_kv_heads * a.num_splits, (rows + 63) / 64);
-  if (a.dtype == 1)
-    hipLaunchKernelGGL((contig_attn_kernel<D, uint16_t>), grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((contig_attn_kernel<D, float>), grid, dim3(256), 0, stream, a);
-  return hipGetLastError();
+  if (a.dtype == 1) return launch_kernel(contig_attn_kernel<D, uint16_t>, grid, dim3(256), a, stream);
+  return launch_kernel(contig_attn_kernel<D, float>, grid, dim3(256), a, stream);
 }
 
 }  // namespace

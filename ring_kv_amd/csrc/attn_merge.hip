@@ -2,6 +2,7 @@
 // output O_s and lse_s over its own keys; with M = max_s lse_s and w_s = exp(lse_s - M) the
 // whole is sum_s w_s O_s / sum_s w_s and lse = M + ln sum_s w_s (a regrouping of the plain
 // softmax over all keys; splits with lse_s = -inf saw no key of a row and carry no weight).
+// A NaN partial (a split that refused its input) makes the row NaN: it is never dropped.
 // The pages split no key range; the split over chunk ranges is this library's way of spreading
 // one long-context verify block over all compute units.
 #include "rkv_device.hpp"
@@ -66,13 +67,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
 #pragma unroll
   for (int u = 0; u < kPre; ++u) {
     const int s = sg + SG * u;
-    const float w = (s < S && lv[u] > -INFINITY) ? expf(lv[u] - Mu) : 0.f;
+    const float w = (s < S && lv[u] != -INFINITY) ? expf(lv[u] - Mu) : 0.f;
     acc += ov[u] * w;
     L += w;
   }
   for (int s = sg + SG * kPre; s < S; s += SG) {
     const float ls = lse[(int64_t)s * rows];
-    const float w = ls > -INFINITY ? expf(ls - Mu) : 0.f;
+    const float w = ls != -INFINITY ? expf(ls - Mu) : 0.f;
     acc += *reinterpret_cast<const f32x4*>(po + s * ostride) * w;
     L += w;
   }
@@ -88,9 +89,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   const int qi = r / a.G;
   const int h = g * a.G + r % a.G;
   *reinterpret_cast<f32x4*>(a.out + ((int64_t)qi * a.n_q_heads + h) * D + d4) =
-      Lt > 0.f ? acc * (1.f / Lt) : f32x4{0.f, 0.f, 0.f, 0.f};
+      Lt != 0.f ? acc * (1.f / Lt) : f32x4{0.f, 0.f, 0.f, 0.f};
   if (a.lse != nullptr && d4 == 0)
-    a.lse[(int64_t)qi * a.n_q_heads + h] = Lt > 0.f ? M + logf(Lt) : -INFINITY;
+    a.lse[(int64_t)qi * a.n_q_heads + h] = Lt != 0.f ? M + logf(Lt) : -INFINITY;
 }
 
 // Many rows, few splits (a prefill block): D/4 threads per row, each owning four consecutive
@@ -117,16 +118,16 @@ __global__ __launch_bounds__(kMergeThreads) void merge_rows_kernel(MergeArgs a) 
   float L = 0.f;
   for (int s = 0; s < S; ++s) {
     const float ls = lse[(int64_t)s * rows];
-    const float w = ls > -INFINITY ? expf(ls - Mu) : 0.f;
+    const float w = ls != -INFINITY ? expf(ls - Mu) : 0.f;
     acc += *reinterpret_cast<const f32x4*>(po + s * ostride) * w;
     L += w;
   }
   const int qi = r / a.G;
   const int h = g * a.G + r % a.G;
   *reinterpret_cast<f32x4*>(a.out + ((int64_t)qi * a.n_q_heads + h) * D + d4) =
-      L > 0.f ? acc * (1.f / L) : f32x4{0.f, 0.f, 0.f, 0.f};
+      L != 0.f ? acc * (1.f / L) : f32x4{0.f, 0.f, 0.f, 0.f};
   if (a.lse != nullptr && d4 == 0)
-    a.lse[(int64_t)qi * a.n_q_heads + h] = L > 0.f ? M + logf(L) : -INFINITY;
+    a.lse[(int64_t)qi * a.n_q_heads + h] = L != 0.f ? M + logf(L) : -INFINITY;
 }
 
 // rows of all KV heads from which the row-parallel form is used (with at most kRowsMaxSplits)
@@ -141,17 +142,13 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
     const int rpb = kMergeThreads / (a.head_dim / 4);
     const dim3 blocks((unsigned)((all_rows + rpb - 1) / rpb));
     if (a.head_dim == 128)
-      hipLaunchKernelGGL(merge_rows_kernel<128>, blocks, dim3(kMergeThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL(merge_rows_kernel<64>, blocks, dim3(kMergeThreads), 0, stream, a);
-    return hipGetLastError();
+      return launch_kernel(merge_rows_kernel<128>, blocks, dim3(kMergeThreads), a, stream);
+    return launch_kernel(merge_rows_kernel<64>, blocks, dim3(kMergeThreads), a, stream);
   }
   const int blocks = (int)all_rows;
   if (a.head_dim == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, dim3(blocks), dim3(kMergeThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(merge_kernel<64>, dim3(blocks), dim3(kMergeThreads), 0, stream, a);
-  return hipGetLastError();
+    return launch_kernel(merge_kernel<128>, dim3(blocks), dim3(kMergeThreads), a, stream);
+  return launch_kernel(merge_kernel<64>, dim3(blocks), dim3(kMergeThreads), a, stream);
 }
 
 }  // namespace rkv

@@ -472,16 +472,13 @@ hipError_t launch_t(const ChunkAttnArgs& a, hipStream_t stream) {
   const int tiles = (rows + 32 * NRG - 1) / (32 * NRG);
   const dim3 blocks(a.n_kv_heads * a.num_splits * tiles);
   const dim3 threads(NRG * KS * 64);
-  if (a.pt != nullptr)
-    hipLaunchKernelGGL((prefill_attn_kernel<D, NRG, KS, true>), blocks, threads, 0, stream, a);
-  else
-    hipLaunchKernelGGL((prefill_attn_kernel<D, NRG, KS, false>), blocks, threads, 0, stream, a);
-  return hipGetLastError();
+  if (a.pt != nullptr) return launch_kernel(prefill_attn_kernel<D, NRG, KS, true>, blocks, threads, a, stream);
+  return launch_kernel(prefill_attn_kernel<D, NRG, KS, false>, blocks, threads, a, stream);
 }
 
 template <int D>
 hipError_t launch_d(const ChunkAttnArgs& a, hipStream_t stream) {
-  const int tile = prefill_tile_rows(a.q_len * a.G, a.n_kv_heads, a.num_splits);
+  const int tile = prefill_tile_rows(a.q_len * a.G, a.n_kv_heads, a.num_splits, a.fill_wgs);
   if (tile == kPrefillTileRows) return launch_t<D, kPrefillTileRows / 32, 1>(a, stream);
   if (tile == kPrefillTileRows / 2) return launch_t<D, kPrefillTileRows / 64, 2>(a, stream);
   return launch_t<D, kPrefillTileRows / 128, 2>(a, stream);

@@ -18,7 +18,12 @@ __global__ __launch_bounds__(256) void scatter_kernel(ScatterArgs a) {
   const int d = (int)(e % a.head_dim);
   const int g = (int)((e / a.head_dim) % a.n_kv_heads);
   const int64_t i = e / ((int64_t)a.head_dim * a.n_kv_heads);
-  const int64_t pos = a.pos_first + i;
+  int64_t pos_first = a.pos_first;
+  if (a.d_pos != nullptr) {
+    pos_first = *a.d_pos;
+    if (pos_first < 0 || pos_first > a.pos_cap) return;
+  }
+  const int64_t pos = pos_first + i;
   int64_t slot, off;
   if (a.pt == nullptr) {
     const int64_t sl = pos % a.ring_size;
@@ -44,8 +49,7 @@ hipError_t launch_scatter(const ScatterArgs& a, hipStream_t stream) {
   const int64_t total = a.n * a.n_kv_heads * a.head_dim;
   if (total == 0) return hipSuccess;
   const int64_t blocks = (total + 255) / 256;
-  hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  return launch_kernel(scatter_kernel, dim3((unsigned)blocks), dim3(256), a, stream);
 }
 
 }  // namespace rkv

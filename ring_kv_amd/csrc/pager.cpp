@@ -5,7 +5,7 @@
 // chunks its rows start, and after the accept commits the rows it keeps; chunks that end up
 // holding no committed position return to the free list.  Whole committed chunks can be paged
 // out to host memory (their slots return to the free list) and back in (same post, same item:
-// cold chunks page to host RAM).
+// chunks move between the pool and host memory).
 #include "ring_kv.h"
 
 #include <algorithm>

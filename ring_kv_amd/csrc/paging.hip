@@ -1,6 +1,6 @@
 // Host paging of the pool: whole 64-token chunks copied between pool slots and a host chunk
 // store, bit-exact (lucebox post "Laguna XS 2.1 33B on a RTX 3090: 296 tok/s peak, 152 tok/s at
-// 256K context", "Three optimizations", item 1: cold chunks page to host RAM).
+// 256K context", "Three optimizations", item 1: chunks move between the pool and host memory).
 //
 // A chunk's K and V are each one contiguous block of n_kv_heads * 64 * head_dim bf16 in a slot,
 // so the copies need no layout change.  Two paths, chosen per batch:
@@ -69,15 +69,13 @@ __global__ __launch_bounds__(kPageThreads) void page_host_kernel(PageHostArgs a)
 hipError_t launch_page_host(const PageHostArgs& a, hipStream_t stream) {
   const int64_t n16 = a.chunk_bytes / 16;
   const int parts = (int)std::min<int64_t>(8, (n16 + kPageThreads - 1) / kPageThreads);
-  hipLaunchKernelGGL(page_host_kernel, dim3(2 * a.n, parts), dim3(kPageThreads), 0, stream, a);
-  return hipGetLastError();
+  return launch_kernel(page_host_kernel, dim3(2 * a.n, parts), dim3(kPageThreads), a, stream);
 }
 
 hipError_t launch_page_copy(const PageArgs& a, hipStream_t stream) {
   const int64_t n16 = a.chunk_bytes / 16;
   const int parts = (int)std::min<int64_t>(8, (n16 + kPageThreads - 1) / kPageThreads);
-  hipLaunchKernelGGL(page_copy_kernel, dim3(2 * a.n, parts), dim3(kPageThreads), 0, stream, a);
-  return hipGetLastError();
+  return launch_kernel(page_copy_kernel, dim3(2 * a.n, parts), dim3(kPageThreads), a, stream);
 }
 
 }  // namespace rkv

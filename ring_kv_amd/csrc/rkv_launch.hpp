@@ -7,6 +7,20 @@
 
 namespace rkv {
 
+// Compute units of the current device (hipDeviceAttributeMultiprocessorCount), queried once per
+// device and cached; 256 (a whole MI355X) where the query fails, e.g. on a machine without a GPU.
+int device_cu_count();
+
+// Launch a kernel that takes one argument struct by value.  hipLaunchKernel returns the status of
+// this launch alone; the thread's last-error state (which may hold an error of some earlier,
+// unrelated HIP call) is neither read nor cleared.
+template <typename A>
+inline hipError_t launch_kernel(void (*fn)(A), dim3 grid, dim3 block, const A& a,
+                                hipStream_t stream) {
+  void* args[] = {const_cast<A*>(&a)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(fn), grid, block, args, 0, stream);
+}
+
 // Most chunks one split may span: positions inside a workgroup are 32-bit offsets from its
 // split's first key.
 constexpr int64_t kMaxSplitChunks = int64_t(1) << 22;
@@ -33,26 +47,31 @@ struct ChunkAttnArgs {
   float* lse;             //                    and lse [q_len][Hq] (may be nullptr)
   float* part_o;          // otherwise partials [Hkv][S][rows][D]
   float* part_lse;        //                    and [Hkv][S][rows]
+  // Device-resident position (nullptr: p0 .. n_chunks above hold).  The block's first row sits
+  // at *d_pos; p0, valid_lo, valid_hi, c_first and n_chunks are derived from it on the device
+  // (pool: context *d_pos + q_len; ring: window span and stored range around it).  A value
+  // outside [0, pos_cap] gives NaN outputs; num_splits * cps covers every value up to pos_cap.
+  const int64_t* d_pos;
+  int64_t pos_cap;
+  int32_t ring_size;      // positions the ring holds (ring only)
+  int32_t fill_wgs;       // workgroups of one round over the device (its compute units)
 };
 // Blocks of up to kVerifyMaxRows rows per KV head (a verify block: q_len * G) run the
-// HBM-streaming kernel with 64-row tiles; longer blocks (batched prefill) run the matrix-core
-// kernel with tiles of kPrefillTileRows rows.  launch_chunk_attn picks the kernel.
+// HBM-streaming kernel with 16-, 32- or 64-row tiles (the smallest whose grid fits one round of
+// fill_wgs workgroups, one per compute unit); longer blocks (batched prefill) run the
+// matrix-core kernel with tiles of kPrefillTileRows rows.  launch_chunk_attn picks the kernel.
 constexpr int kVerifyMaxRows = 256;
-// One round of verify workgroups (one per compute unit): the row tile is the smallest whose grid
-// fits it.
-constexpr int kVerifyFillWorkgroups = 256;
 constexpr int kPrefillTileRows = 256;
 // Row tile of the prefill kernel: kPrefillTileRows, or half of it (two waves per row group, one
 // per half of each chunk's keys) when the full tiles would leave most of the chip without a
-// workgroup (fewer than kPrefillFillWorkgroups), or a quarter of it (two row groups) where even
-// that grid of quarter tiles fits one round of kPrefillFillWorkgroups (a block over the ring).
-constexpr int kPrefillFillWorkgroups = 256;
-inline int prefill_tile_rows(int rows, int n_kv_heads, int num_splits) {
+// workgroup (fewer than `fill`, the compute units), or a quarter of it (two row groups) where
+// even that grid of quarter tiles fits one round of `fill` workgroups (a block over the ring).
+inline int prefill_tile_rows(int rows, int n_kv_heads, int num_splits, int fill) {
   auto grid = [&](int tile) {
     return (int64_t)n_kv_heads * num_splits * ((rows + tile - 1) / tile);
   };
-  if (grid(kPrefillTileRows) >= kPrefillFillWorkgroups) return kPrefillTileRows;
-  if (grid(kPrefillTileRows / 4) <= kPrefillFillWorkgroups) return kPrefillTileRows / 4;
+  if (grid(kPrefillTileRows) >= fill) return kPrefillTileRows;
+  if (grid(kPrefillTileRows / 4) <= fill) return kPrefillTileRows / 4;
   return kPrefillTileRows / 2;
 }
 hipError_t launch_chunk_attn(const ChunkAttnArgs& a, hipStream_t stream);
@@ -103,6 +122,13 @@ struct AcceptArgs {
 };
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream);
 
+// *pos += *accept_len + 1 on the device (one decode step's committed tokens).
+struct AdvanceArgs {
+  int64_t* pos;
+  const int32_t* accept_len;
+};
+hipError_t launch_advance(const AdvanceArgs& a, hipStream_t stream);
+
 struct ScatterArgs {
   const uint16_t* k_src;  // [n][Hkv][D]
   const uint16_t* v_src;
@@ -119,6 +145,10 @@ struct ScatterArgs {
   int32_t* pt_w;          // nullptr: no table writes
   int32_t first_new, n_new;
   int32_t new_slots[RKV_MAX_APPEND_CHUNKS];
+  // device-resident first position (nullptr: pos_first holds); a value outside [0, pos_cap]
+  // writes nothing
+  const int64_t* d_pos;
+  int64_t pos_cap;
 };
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t stream);
 

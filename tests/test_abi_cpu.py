@@ -235,3 +235,42 @@ def test_resident_workspace_is_that_of_its_chunks():
     # chunks 8..38 resident plus the block's chunk 39: a packed context of 32 chunks
     assert L.verify_attn_paged_resident(d, P, P, P, P, _i32(*range(8, 40)), 32, 160, 2560, 0,
                                         P, short, P, NULL, NULL) == EWS
+
+
+def test_device_position_checks():
+    """The calls that read the block's position from device memory refuse on the host what the
+    position-argument calls refuse, plus a null position, a negative cap and prefill-sized
+    blocks; their split layout and workspace are those of the largest position."""
+    ws_ring = L.verify_attn_ring_workspace_bytes(dims(), 2048, 512, 0)
+    rd = lambda d=None, pos=P, cap=200000, size=2048, window=512, splits=0, ws=P, wsb=ws_ring, out=P: \
+        L.verify_attn_ring_dev(dims() if d is None else d, P, P, P, pos, cap, size, window,  # noqa: E731
+                               splits, ws, wsb, out, NULL, NULL)
+    assert rd(pos=NULL) == ENULL and rd(out=NULL) == ENULL
+    assert rd(cap=-1) == EARG and rd(window=0) == EARG and rd(splits=-1) == EARG
+    assert rd(size=512) == ERING and rd(size=2000) == ERING
+    assert rd(d=dims(dtype=0)) == EDTYPE
+    assert rd(d=dims(q_len=65)) == ESHAPE                 # 260 rows per KV head: prefill-sized
+    assert rd(ws=NULL) == EWS and rd(wsb=ws_ring - 1) == EWS
+    cap = 131056
+    ws_pool = L.verify_attn_paged_workspace_bytes(dims(), cap + 16, 64, 0)
+    pd = lambda d=None, pos=P, cap=cap, n_table=2048, chunk=64, ws=P, wsb=ws_pool: \
+        L.verify_attn_paged_dev(dims() if d is None else d, P, P, P, P, n_table, 2048, chunk,  # noqa: E731
+                                pos, cap, 0, ws, wsb, P, NULL, NULL)
+    assert pd(pos=NULL) == ENULL and pd(d=None) != ENULL
+    assert L.verify_attn_paged_dev(None, P, P, P, P, 2048, 2048, 64, P, cap, 0, P, ws_pool, P,
+                                   NULL, NULL) == ENULL
+    assert pd(cap=-1) == EARG
+    assert pd(cap=cap + 1) == ETABLE                      # position 131,072 needs entry 2,048
+    assert pd(chunk=32) == ETABLE
+    assert pd(d=dims(q_len=65), cap=cap - 64) == ESHAPE
+    assert pd(ws=NULL) == EWS and pd(wsb=ws_pool - 1) == EWS
+    ar = lambda n=16, pos=P, cap=100, size=2048: L.verify_kv_append_ring_dev(  # noqa: E731
+        P, P, n, pos, cap, 4, 128, P, P, size, NULL)
+    assert ar(pos=NULL) == ENULL and ar(cap=-1) == EARG and ar(n=0) == EARG
+    assert ar(n=1025) == EARG and ar(size=100) == ERING
+    ap = lambda n=16, pos=P, cap=100, n_table=2, table=P: L.verify_kv_append_paged_dev(  # noqa: E731
+        P, P, n, pos, cap, 4, 128, P, P, table, n_table, 8, NULL)
+    assert ap(pos=NULL) == ENULL and ap(table=NULL) == ENULL and ap(cap=-1) == EARG
+    assert ap(cap=113) == ETABLE                          # 113 + 16 - 1 = 128: chunk 2
+    assert L.verify_pos_advance(NULL, P, NULL) == ENULL
+    assert L.verify_pos_advance(P, NULL, NULL) == ENULL

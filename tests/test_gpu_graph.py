@@ -1,16 +1,99 @@
 """Entry points captured in HIP graphs and replayed (a verify step; prefill blocks, the resident
 call and host paging):
 every replay must reproduce the eager results bit for bit, with eager work and
-synchronisations between the replays; and one accept workspace serves many calls in a row."""
+synchronisations between the replays; and one accept workspace serves many calls in a row.
+The whole 40-layer step at context 131,072 plus its accept, captured in one graph, is checked
+replay by replay against the fp64 oracle."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import ring_kv_amd as rk
-from synth import accept_case, paged_case, ring_case
-from gpu_util import dev, say
+from ring_kv_amd._lib import AttnDims
+from synth import STACK_LAYERS, accept_case, paged_case, ring_case, workload
+from gpu_util import REL_BF16, TOL_BF16, TOL_LSE_BF16, dev, run_oracle, say
 
 pytestmark = pytest.mark.gpu
+
+
+def test_graph_replay_stack_40l_131k_against_oracle():
+    """The 40-layer step (30 window layers over the 2,048-slot ring at position 131,056, 10
+    full-attention layers over permuted pools at context 131,072) and the greedy accept over
+    [17 x 65,536] logits, captured in ONE HIP graph and replayed three times, every output
+    clobbered by eager work between replays.  After each replay every layer's out and lse are
+    compared with the fp64 oracle (bf16 tolerances) and the accept length and committed tokens
+    exactly."""
+    L = rk.lib()
+    dims = AttnDims(16, 16, 4, 128, 0.0, 1)
+    ws_p = torch.empty(L.verify_attn_paged_workspace_bytes(ctypes.byref(dims), 131072, 64, 0),
+                       dtype=torch.uint8, device="cuda")
+    ws_r = torch.empty(L.verify_attn_ring_workspace_bytes(ctypes.byref(dims), 2048, 512, 0),
+                       dtype=torch.uint8, device="cuda")
+    layers, refs = [], []
+    acc = None
+    for l in range(STACK_LAYERS):
+        c, acc = workload("stack_40l_131k", l, keep_rows=False)
+        d = dict(kind=c.kind, q=dev(c.q), out=torch.empty(16, 16, 128, device="cuda"),
+                 lse=torch.empty(16, 16, device="cuda"))
+        if c.kind == "ring":
+            d.update(k=dev(c.k_ring), v=dev(c.v_ring), pos0=c.pos0, window=c.window)
+        else:
+            d.update(k=dev(c.k_pool), v=dev(c.v_pool), pt=dev(c.page_table), ctx=c.ctx_len)
+        refs.append(run_oracle(c))
+        layers.append(d)
+        if l % 8 == 7:
+            say(f"stack graph: layer {l} built, oracle done")
+        del c
+    lg, pr = dev(acc.logits), dev(acc.proposals)
+    ra, rcom, rt = oracle.greedy_accept(acc.logits, acc.proposals)
+    assert ra == acc.planted_accept
+    wsa = torch.zeros(L.verify_accept_workspace_bytes(16, 65536), dtype=torch.uint8, device="cuda")
+    a_len = torch.empty(1, dtype=torch.int32, device="cuda")
+    com = torch.empty(17, dtype=torch.int32, device="cuda")
+    amax = torch.empty(17, dtype=torch.int32, device="cuda")
+
+    def step():
+        for d in layers:
+            if d["kind"] == "ring":
+                rk.verify_attn_ring(d["q"], d["k"], d["v"], d["pos0"], d["window"], out=d["out"],
+                                    lse=d["lse"], workspace=ws_r)
+            else:
+                rk.verify_attn_paged(d["q"], d["k"], d["v"], d["pt"], d["ctx"], out=d["out"],
+                                     lse=d["lse"], workspace=ws_p)
+        rk.verify_accept(lg, pr, accept_len=a_len, committed=com, row_argmax=amax, workspace=wsa)
+
+    g = torch.cuda.CUDAGraph()
+    say("stack graph: capture")
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for d in layers:
+            d["out"].fill_(float("nan"))                 # eager work between replays
+            d["lse"].fill_(float("nan"))
+        a_len.fill_(-1)
+        com.fill_(-7)
+        amax.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        worst = (0.0, 0.0)
+        for l, (d, (o_ref, l_ref)) in enumerate(zip(layers, refs)):
+            out, lse = d["out"].cpu().numpy(), d["lse"].cpu().numpy()
+            assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse)), f"replay {rep} layer {l}"
+            err, lerr = float(np.abs(out - o_ref).max()), float(np.abs(lse - l_ref).max())
+            assert err <= TOL_BF16 and err <= REL_BF16 * np.abs(o_ref).max(), \
+                f"replay {rep} layer {l} ({d['kind']}): max abs error {err}"
+            assert lerr <= TOL_LSE_BF16, f"replay {rep} layer {l}: lse error {lerr}"
+            worst = (max(worst[0], err), max(worst[1], lerr))
+        a = int(a_len.cpu()[0])
+        assert a == ra, f"replay {rep}: accept length {a}, oracle {ra}"
+        assert list(com.cpu().numpy()) == list(rcom) + [-1] * (16 - ra)
+        assert list(amax.cpu().numpy()) == list(rt)
+        say(f"stack graph: replay {rep}: max|err| out {worst[0]:.2e}, lse {worst[1]:.2e}, "
+            f"accept {a} exact")
 
 
 def test_accept_workspace_reused_many_times():
