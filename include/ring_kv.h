@@ -180,6 +180,23 @@ int32_t verify_attn_paged(const rkv_attn_dims* dims, const void* q, const void* 
                           int32_t num_splits, void* workspace, size_t workspace_bytes,
                           float* out, float* lse, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): verify_attn_paged with no workspace argument.  The
+ * split partials go to a static device array inside the library, RKV_NOALLOC_SCRATCH_BYTES
+ * (16 MiB) per device, held from the first call on a device until the process ends; the call
+ * itself allocates nothing.  Same arguments (minus the workspace), kernels, splits and results
+ * as verify_attn_paged.  RKV_ERR_WORKSPACE when the call's partials,
+ * verify_attn_paged_workspace_bytes(dims, ctx_len, 64, num_splits) bytes, exceed the array
+ * (4 KV heads x 64 splits x 64 rows fit: every verify block of the named workloads; a
+ * 1,024-token prefill block does not); RKV_ERR_HIP if the array's address cannot be found.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU (on different
+ * streams, or from different threads) race on it; calls ordered on one stream do not. */
+#define RKV_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int32_t verify_attn_paged_noalloc(const rkv_attn_dims* dims, const void* q, const void* k_pool,
+                                  const void* v_pool, const int32_t* page_table, int32_t n_table,
+                                  int32_t n_slots, int32_t chunk_size, int64_t ctx_len,
+                                  int32_t num_splits, float* out, float* lse, void* stream);
+
 /* Split count verify_attn_paged uses for num_splits = 0 (host-only, no HIP call). */
 int32_t verify_attn_paged_auto_splits(const rkv_attn_dims* dims, int64_t ctx_len,
                                       int32_t chunk_size);

@@ -43,6 +43,8 @@ _PROTOS = {
     "verify_attn_paged": (c_int32, [_DIMS, _P, _P, _P, _P, c_int32, c_int32, c_int32, c_int64,
                                     c_int32, _P, c_size_t, _P, _P, _P]),
     "verify_attn_paged_auto_splits": (c_int32, [_DIMS, c_int64, c_int32]),
+    "verify_attn_paged_noalloc": (c_int32, [_DIMS, _P, _P, _P, _P, c_int32, c_int32, c_int32,
+                                            c_int64, c_int32, _P, _P, _P]),
     "verify_attn_paged_partial": (c_int32, [_DIMS, _P, _P, _P, _P, c_int32, c_int32, c_int32,
                                             c_int64, c_int32, _P, _P, _P]),
     "attn_merge_partials": (c_int32, [_DIMS, c_int32, _P, _P, _P, _P, _P]),

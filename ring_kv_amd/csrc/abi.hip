@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/ring_kv.h"
 #include "rkv_launch.hpp"
@@ -386,6 +387,56 @@ int32_t verify_attn_paged(const rkv_attn_dims* dims, const void* q, const void* 
       (workspace == nullptr || workspace_bytes < partial_bytes(dims, a.num_splits)))
     return RKV_ERR_WORKSPACE;
   return run_chunk_attn(a, dims, workspace, out, lse, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Split partials of verify_attn_paged_noalloc: a file-scope device array, one copy per device the
+// library runs on, held until the process ends.  Its name is a host-side stand-in in host code;
+// kernels get the device address hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = RKV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of `scratch` on the current device, looked up once per device (with that
+// device current); nullptr if the lookup fails.
+void* scratch_address() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t verify_attn_paged_noalloc(const rkv_attn_dims* dims, const void* q, const void* k_pool,
+                                  const void* v_pool, const int32_t* page_table, int32_t n_table,
+                                  int32_t n_slots, int32_t chunk_size, int64_t ctx_len,
+                                  int32_t num_splits, float* out, float* lse, void* stream) {
+  int32_t st = check_paged(dims, q, k_pool, v_pool, page_table, n_table, n_slots, chunk_size,
+                           ctx_len);
+  if (st != RKV_OK) return st;
+  if (out == nullptr) return RKV_ERR_NULL;
+  if (num_splits < 0) return RKV_ERR_ARG;
+  ChunkAttnArgs a = paged_args(dims, q, k_pool, v_pool, page_table, n_slots, ctx_len);
+  choose_splits(a.n_chunks, paged_split_target(dims, a.n_chunks), num_splits, &a.num_splits,
+                &a.cps);
+  if (a.num_splits > 1 && partial_bytes(dims, a.num_splits) > kScratchBytes)
+    return RKV_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (a.num_splits > 1 && (ws = scratch_address()) == nullptr) return RKV_ERR_HIP;
+  return run_chunk_attn(a, dims, ws, out, lse, static_cast<hipStream_t>(stream));
 }
 
 int32_t verify_attn_paged_resident(const rkv_attn_dims* dims, const void* q,
