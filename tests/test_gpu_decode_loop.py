@@ -95,7 +95,7 @@ def test_one_graph_replayed_over_decode_steps():
     d_pos = torch.tensor([P0], dtype=torch.int64, device="cuda")
     L = rk.lib()
     dims = AttnDims(Q, HQ, HKV, D, 0.0, 1)
-    ws_r = torch.empty(L.verify_attn_ring_workspace_bytes(ctypes.byref(dims), R, W, 0),
+    ws_r = torch.zeros(L.verify_attn_ring_workspace_bytes(ctypes.byref(dims), R, W, 0),
                        dtype=torch.uint8, device="cuda")
     ws_p = torch.empty(L.verify_attn_paged_workspace_bytes(ctypes.byref(dims), pos_cap + Q, CH, 0),
                        dtype=torch.uint8, device="cuda")
@@ -225,8 +225,10 @@ def test_device_position_outside_the_cap():
 
 def test_launch_status_ignores_an_earlier_error():
     """An error some earlier HIP call left in the thread's last-error state is not reported by
-    a good call of the library (its status is the launch's own) and is still there afterwards
-    for its owner to read."""
+    a good call of the library: its status is the launch's own.  (Whether the error is still
+    there afterwards is the HIP runtime's business: the library neither reads nor clears it.)
+    Every buffer is allocated before the error is planted, so that no torch work runs between
+    the error and the call (torch checks the last error after its own launches)."""
     # the HIP runtime this process already runs (the one torch loaded and the library uses)
     path = next(ln.split()[-1] for ln in open("/proc/self/maps") if "libamdhip64" in ln)
     hip = ctypes.CDLL(path)
@@ -234,12 +236,17 @@ def test_launch_status_ignores_an_earlier_error():
     hip.hipSetDevice.argtypes = [ctypes.c_int]
     c = ring_case(65, 0, 30000, Q, HQ, HKV, D, R, W, keep_rows=False)
     q, kr, vr = dev(c.q), dev(c.k_ring), dev(c.v_ring)
+    dims = AttnDims(Q, HQ, HKV, D, 0.0, 1)
+    ws = torch.zeros(rk.lib().verify_attn_ring_workspace_bytes(ctypes.byref(dims), R, W, 0),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty(Q, HQ, D, device="cuda")
+    lse = torch.empty(Q, HQ, device="cuda")
     torch.cuda.synchronize()
     hip.hipGetLastError()                              # start from a clean state
     assert hip.hipSetDevice(9999) != 0                 # an invalid device: an error, nothing else
-    out, lse = rk.verify_attn_ring(q, kr, vr, 30000, W)   # raises if the status is not RKV_OK
+    rk.verify_attn_ring(q, kr, vr, 30000, W, out=out, lse=lse, workspace=ws)   # raises unless OK
+    left = hip.hipGetLastError()                       # consumed here, before any torch work
+    say(f"last error after the library call: {left}")
     torch.cuda.synchronize()
     want = oracle.attention_ring(c.q, c.k_ring, c.v_ring, 30000, 30000 % R, R, W)
     _close((out.cpu().numpy(), lse.cpu().numpy()), want, "ring after an earlier error")
-    left = hip.hipGetLastError()
-    say(f"last error after the library call: {left}")
