@@ -112,6 +112,78 @@ def event_ms(fn, n, torch):
     return s.elapsed_time(e) / n
 
 
+def capture(fn, torch):
+    """fn captured in a HIP graph (after one run on a side stream, as torch recommends)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def per_call_ms(fn, n, torch):
+    """ms of each of n calls: HIP events recorded around every call."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    torch.cuda.synchronize()
+    for s, e in ev:
+        s.record()
+        fn()
+        e.record()
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) for s, e in ev]
+
+
+def pct(xs, q):
+    """q-th percentile (0..100) of a list, linear interpolation."""
+    import numpy as np
+    return float(np.percentile(np.asarray(xs, dtype=float), q))
+
+
+def dist(xs, nd=2):
+    return {"median": round(pct(xs, 50), nd), "p10": round(pct(xs, 10), nd),
+            "p90": round(pct(xs, 90), nd), "n": len(xs)}
+
+
+def kernel_times(torch, fn, n, pre=None, skip="read_probe"):
+    """The device's own kernel durations, from the HIP kernel records the in-process profiler
+    (torch.profiler over roctracer) collects: fn is called n times, pre() before each call (its
+    kernels, named like `skip`, are not counted).  Returns (per-call sums of the durations of the
+    call's kernels in µs, {kernel name: [durations µs]}).  These are the same per-dispatch
+    durations a rocprofv3 kernel trace reports; launch gaps are not in them."""
+    from torch.autograd import DeviceType
+    from torch.profiler import ProfilerActivity, profile
+    torch.cuda.synchronize()
+    with profile(activities=[ProfilerActivity.CUDA]) as prof:
+        for _ in range(n):
+            if pre is not None:
+                pre()
+            fn()
+        torch.cuda.synchronize()
+    evs = [e for e in prof.events() if e.device_type == DeviceType.CUDA and skip not in e.name]
+    evs.sort(key=lambda e: e.time_range.start)
+    dur = lambda e: getattr(e, "device_time", None) or e.cuda_time  # noqa: E731
+    by_name = {}
+    for e in evs:
+        by_name.setdefault(e.name, []).append(dur(e))
+    if n == 0 or len(evs) % n:
+        return [], by_name
+    k = len(evs) // n
+    return [sum(dur(e) for e in evs[i * k:(i + 1) * k]) for i in range(n)], by_name
+
+
+def short_name(name):
+    """`chunk_attn_kernel<128, 4, 2, true>` from a demangled kernel name."""
+    import re
+    m = re.search(r"(\w+_kernel(?:<[^>]*>)?)", name)
+    return m.group(1) if m else name[:60]
+
+
 class Stack:
     """Device-resident inputs, outputs and workspaces of the 40-layer verify step."""
 
@@ -188,6 +260,50 @@ class Stack:
                                                   self.splits, part_out=self.part_o,
                                                   part_lse=self.part_l)
 
+    def decode_setup(self, steps):
+        """The decode loop over this step's stores: every layer appends the block's 16 K/V rows
+        at the device-resident position, attends, then the accept and the on-device advance by
+        a + 1 (the planted agreement of the step's logits).  It starts early enough that `steps`
+        replays stay inside the pools (whose tables cover positions up to 131,071) and ends at
+        131,056 at the latest.  It writes into the stores: run it after the step's parity."""
+        torch = self.torch
+        self.adv = self.accept.planted_accept + 1
+        self.pos_cap = 131072 - 16
+        self.pos_first = self.pos_cap - self.adv * steps
+        self.d_pos = torch.tensor([self.pos_first], dtype=torch.int64, device="cuda")
+        g = torch.Generator(device="cuda").manual_seed(11)
+        for d in self.layers:
+            d["k_new"] = torch.randn((16, 4, 128), device="cuda", generator=g).to(torch.bfloat16)
+            d["v_new"] = torch.randn((16, 4, 128), device="cuda", generator=g).to(torch.bfloat16)
+        L = self.rk.lib()
+        from ring_kv_amd._lib import AttnDims
+        import ctypes
+        dims = AttnDims(16, 16, 4, 128, 0.0, 1)
+        self.ws_paged_dev = torch.empty(max(1, L.verify_attn_paged_workspace_bytes(
+            ctypes.byref(dims), self.pos_cap + 16, 64, 0)), dtype=torch.uint8, device="cuda")
+
+    def decode_step(self):
+        rk, cap, dp = self.rk, self.pos_cap, self.d_pos
+        for d in self.layers:
+            if d["kind"] == "ring":
+                rk.verify_kv_append_ring_dev(d["k_new"], d["v_new"], dp, cap, d["k"], d["v"])
+                rk.verify_attn_ring_dev(d["q"], d["k"], d["v"], dp, cap, d["window"], out=d["out"],
+                                        lse=d["lse"], workspace=self.ws_ring)
+            else:
+                rk.verify_kv_append_paged_dev(d["k_new"], d["v_new"], dp, cap, d["k"], d["v"],
+                                              d["pt"])
+                rk.verify_attn_paged_dev(d["q"], d["k"], d["v"], d["pt"], dp, cap, out=d["out"],
+                                         lse=d["lse"], workspace=self.ws_paged_dev)
+        rk.verify_accept(self.logits, self.prop, accept_len=self.acc_len, committed=self.committed,
+                         row_argmax=self.argmax, workspace=self.ws_acc)
+        rk.verify_pos_advance(dp, self.acc_len)
+
+    def decode_kv_bytes(self, pos):
+        """KV bytes the decode step at block position `pos` attends: 30 window spans of 527
+        positions and 10 pools of pos + 16 positions, 2,048 B per position (K and V, 4 KV heads,
+        D 128, bf16)."""
+        return 30 * 527 * 2048 + 10 * (pos + 16) * 2048
+
 
 def attn_flops(c):
     """QK^T + PV flops of an attention case, counting exactly the keys each query sees."""
@@ -224,8 +340,9 @@ def config_timings(torch, rk, synth, probe, n_small, n_large):
     times in one HIP graph: warm = back-to-back calls; cold (calls of 20 µs and more) = every call
     preceded by a 512 MiB streaming read that evicts L2 and the last-level cache without dirtying
     them, minus a graph of the reads alone; the 256K pool also rotates over three copies.  Mean
-    µs per call; per-dispatch distributions, cold, come from the kernel trace of
-    `bench.py --mode configs`."""
+    µs per call, launch gaps included.  Beside them, the device's own kernel time per call (the
+    call's kernel durations summed, from the in-process kernel records), warm and cold: median,
+    p10, p90 over 30 calls."""
     t = lambda a: rk.tensor_from_numpy(a, "cuda")  # noqa: E731
     scratch = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
     flush = lambda: probe.read(scratch)  # noqa: E731
@@ -247,6 +364,18 @@ def config_timings(torch, rk, synth, probe, n_small, n_large):
         n = n // len(fns) * len(fns)
         warm = graph_ms(op, n, 3, torch) * 1e3
         e = {"us_warm": round(warm, 2), "calls_per_graph": n, "note": note}
+        # the device's own kernel time per call (the sum of the call's kernel durations, as a
+        # kernel trace gives them): back to back (warm) and after a cache-evicting read (cold)
+        m = min(n, 30)
+        kw, _ = kernel_times(torch, op, m)
+        kc, _ = kernel_times(torch, op, m, pre=flush)
+        if kw and kc:
+            e["kernel_us_warm"] = dist(kw)
+            e["kernel_us_cold"] = dist(kc)
+            if nbytes and e["kernel_us_cold"]["median"] > 0:
+                kmed = e["kernel_us_cold"]["median"]
+                e["gbps_kernel_cold"] = round(nbytes / (kmed * 1e-6) / 1e9, 1)
+                e["hbm_frac_kernel_cold"] = round(e["gbps_kernel_cold"] / HBM_PEAK_GBPS, 4)
         t, which = warm, "warm"
         if warm >= 20.0:
             # the difference of two graphs resolves only calls well above the launch overlap;
@@ -315,6 +444,19 @@ def config_timings(torch, rk, synth, probe, n_small, n_large):
     entry("append_paged_16", [lambda: rk.verify_kv_append_paged(kb, vb, 131064, kp, vp, table,
                                                                 2048, [2047])], n_small,
           2 * kb.numel() * 2, 0, 0, "", "verify_kv_append_paged, 16 rows starting one chunk")
+    # a 1,024-token prefill block's rows appended (4 KV heads, D 128: 2 MiB of K and V)
+    kb1 = torch.randn((1024, 4, 128), device="cuda", generator=g).to(torch.bfloat16)
+    vb1 = torch.randn((1024, 4, 128), device="cuda", generator=g).to(torch.bfloat16)
+    entry("append_ring_1024", [lambda: rk.verify_kv_append_ring(kb1, vb1, 130048, kr, vr)], n_small,
+          2 * kb1.numel() * 2, 0, 0, "", "verify_kv_append_ring, 1,024 rows")
+    new16 = list(range(2032, 2048))
+    entry("append_paged_1024", [lambda: rk.verify_kv_append_paged(kb1, vb1, 130048, kp, vp, table,
+                                                                  2032, new16)], n_small,
+          2 * kb1.numel() * 2, 0, 0, "", "verify_kv_append_paged, 1,024 rows starting 16 chunks")
+    copy_src = torch.empty(2 << 20, dtype=torch.uint8, device="cuda")
+    copy_dst = torch.empty_like(copy_src)
+    entry("copy_2mib", [lambda: copy_dst.copy_(copy_src)], n_small, 2 * (2 << 20), 0, 0, "",
+          "a plain 2 MiB device copy (torch), for comparison with the 1,024-row appends")
     pager = rk.Pager(4096, 4096)
     t0 = time.perf_counter()
     for i in range(2000):
@@ -773,7 +915,6 @@ def main():
     if args.workload == "stack_40l_131k":
         log("building the 40-layer step inputs")
         st = Stack(torch, rk, synth)
-        step_bytes = st.kv_bytes + st.accept_bytes
         for _ in range(args.warmup):
             st.step()
         torch.cuda.synchronize()
@@ -782,28 +923,35 @@ def main():
         ms = eager_ms
         graph = False
         if not args.no_graph:
-            g = torch.cuda.CUDAGraph()
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(side):
-                st.step()
-            torch.cuda.current_stream().wait_stream(side)
-            torch.cuda.synchronize()
-            with torch.cuda.graph(g):
-                st.step()
+            g = capture(st.step, torch)
             for _ in range(args.warmup):
                 g.replay()
             torch.cuda.synchronize()
+            # the timed region: exactly `steps` replays between two synchronisations
             ms = event_ms(g.replay, args.steps, torch)
             graph = True
             log(f"graph step {ms:.3f} ms")
-        # dominant kernel: the paged split-K kernel at 131,072 over the 10 paged layers, one
-        # round of 10 launches captured in a HIP graph; HIP events on the replay stream
+            step_fn = g.replay
+        else:
+            step_fn = st.step
+        # the step's distribution: events around each replay; the device's kernel time per step
+        # (the sum of its 82 kernels' durations) from the in-process kernel records
+        per_step = per_call_ms(step_fn, args.steps, torch)
+        k_step, k_by = kernel_times(torch, step_fn, min(5, args.steps))
+        # dominant kernel: the paged split-K kernel at 131,072 over the 10 paged layers, three
+        # rounds of 10 launches in one HIP graph; HIP events on the replay stream (launch gaps
+        # included), and the kernels' own durations from the kernel records of the same replays
         st.paged_partial_round()
-        k_ms = graph_ms(st.paged_partial_round, 2, max(3, args.steps // 2), torch) / 10
+        gk = capture(lambda: [st.paged_partial_round() for _ in range(3)], torch)
+        k_ms = event_ms(gk.replay, max(3, args.steps // 4), torch) / 30
+        _, k_dom = kernel_times(torch, gk.replay, 2)
+        dom = [v for n, v in k_dom.items() if "chunk_attn_kernel" in n]
+        k_us = dom[0] if len(dom) == 1 else []
         per_launch = 2 * 131072 * 4 * 128 * 2
         achieved = per_launch / (k_ms * 1e-3) / 1e9
-        log(f"paged split kernel {k_ms * 1e3:.1f} us/launch, {achieved:.0f} GB/s")
+        kern_mean = sum(k_us) / len(k_us) if k_us else None
+        log(f"paged split kernel {k_ms * 1e3:.1f} us/launch (events), "
+            f"{kern_mean if kern_mean is None else round(kern_mean, 2)} us (kernel records)")
         # the step by layer type, each type captured alone (30 ring layers, 10 paged, accept)
         ring_us = graph_ms(st.ring_round, 1, max(3, args.steps // 2), torch) * 1e3 / 30
         paged_us = graph_ms(st.paged_round, 1, max(3, args.steps // 2), torch) * 1e3 / 10
@@ -813,10 +961,15 @@ def main():
                                     "accept_17x65536": round(acc_us, 2),
                                     "sum_40_layers_and_accept": round(30 * ring_us + 10 * paged_us
                                                                       + acc_us, 1)}
+        kv_gbps = st.kv_bytes / (ms * 1e-3) / 1e9
         res.update({
-            "value": round(step_bytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+            "value": round(kv_gbps, 2), "unit": "GB/s",
             "ms_per_step": round(ms, 4), "eager_ms_per_step": round(eager_ms, 4),
-            "hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "hbm_frac": round(kv_gbps / HBM_PEAK_GBPS, 4),
+            "step_ms": dist(per_step, 4),
+            "step_kernel_ms": dist([x / 1e3 for x in k_step], 4) if k_step else None,
+            "step_kernels_us": {short_name(n): dist(v) for n, v in k_by.items()},
+            "with_logits_gbps": round((st.kv_bytes + st.accept_bytes) / (ms * 1e-3) / 1e9, 2),
             "config": {"workload": "stack_40l_131k", "layers": 40, "ring_layers": 30,
                        "paged_layers": 10, "q_len": 16, "n_q_heads": 16, "n_kv_heads": 4,
                        "head_dim": 128, "ring_size": 2048, "window": 512, "paged_ctx": 131072,
@@ -826,12 +979,39 @@ def main():
                          "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBPS, 4),
                          "us_per_launch": round(k_ms * 1e3, 2),
+                         "kernel_us": round(kern_mean, 2) if kern_mean else None,
+                         "kernel_us_dist": dist(k_us) if k_us else None,
+                         "frac_kernel": round(per_launch / (kern_mean * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
+                         if kern_mean else None,
                          "algorithmic_bytes_per_launch": per_launch,
                          "traffic": traffic_entry(per_launch)},
         })
         step_out = {l: (st.layers[l]["out"].cpu().numpy(), st.layers[l]["lse"].cpu().numpy())
                     for l in (0, 1, 2, 3)}
         step_out["accept"] = (int(st.acc_len.cpu()[0]), st.committed.cpu().numpy())
+        if not args.no_graph:
+            # the decode loop: one captured step (appends + attention + accept + advance, the
+            # block position on the device) replayed as the context grows
+            n_dec = args.warmup + args.steps + 1
+            st.decode_setup(n_dec)
+            gd = capture(st.decode_step, torch)      # the capture's warm-up run advances once
+            for _ in range(args.warmup):
+                gd.replay()
+            torch.cuda.synchronize()
+            p_start = int(st.d_pos.cpu()[0])
+            dec = per_call_ms(gd.replay, args.steps, torch)
+            p_end = int(st.d_pos.cpu()[0])
+            assert p_end - p_start == args.steps * st.adv and p_end <= st.pos_cap + st.adv
+            dec_bytes = sum(st.decode_kv_bytes(p_start + i * st.adv) for i in range(args.steps))
+            dec_ms = sum(dec) / len(dec)
+            log(f"decode step with appends {dec_ms:.3f} ms")
+            res["step_with_appends"] = {
+                "ms_per_step": round(dec_ms, 4), "step_ms": dist(dec, 4),
+                "kv_gbps": round(dec_bytes / args.steps / (dec_ms * 1e-3) / 1e9, 1),
+                "positions": [p_start, p_end - st.adv], "advance_per_step": st.adv,
+                "note": "one captured graph replayed as the decode loop: per layer the block's "
+                        "16 K/V rows appended at the device-resident position, then attention; "
+                        "the accept and the on-device advance by a + 1"}
         del st
         torch.cuda.empty_cache()
 
@@ -908,12 +1088,18 @@ def main():
         res["configs_gpu"] = config_timings(torch, rk, synth, probe, 100, 30)
         res["read_bw_probe"] = read_bw_probe(torch, probe)
         if "us_per_layer_256k" in res:
-            # the headline 256K figure is the cold one (caches evicted before each call); the
-            # back-to-back graph figure stays alongside (it runs into the card's power limit)
-            cold = res["configs_gpu"]["paged_256k"]["us_cold"]
+            # The headline 256K figure: the layer's two kernels (split + merge), their own
+            # durations summed per call, caches evicted before each call (median of 30 calls
+            # over three pool copies).  Alongside: the cold graph figure (calls in a graph minus a
+            # graph of the evicting reads: launch gaps included) and the back-to-back graph
+            # figure (long series of this kernel reach the card's power limit).
+            c256 = res["configs_gpu"]["paged_256k"]
             kv256 = 2 * 262144 * 4 * 128 * 2
             res["us_per_layer_256k_back_to_back"] = res["us_per_layer_256k"]
+            res["us_per_layer_256k_graph_cold"] = c256["us_cold"]
+            cold = c256["kernel_us_cold"]["median"] if "kernel_us_cold" in c256 else c256["us_cold"]
             res.update({"us_per_layer_256k": cold,
+                        "us_per_layer_256k_dist": c256.get("kernel_us_cold"),
                         "kv_gbps_256k": round(kv256 / (cold * 1e-6) / 1e9, 1),
                         "hbm_frac_256k": round(kv256 / (cold * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
                         "hbm_frac_256k_of_read_probe": round(
