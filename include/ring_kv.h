@@ -253,8 +253,8 @@ int32_t verify_accept(const float* logits, int32_t n_draft, int32_t vocab,
  * post, "3. Ring caches for the sliding-window layers": slot = pos mod 2048); the pool
  * puts it in chunk p / 64 at offset p mod 64, the chunk living in slot page_table[p/64]
  * ("Three optimizations", item 1: 64-token chunks).  This is also how a verify block's
- * own rows are appended before attention.  All pointers are caller-owned device memory;
- * dtype must be bf16.  For the ring, n <= ring_size (RKV_ERR_RING otherwise); for the
+ * own rows are appended before attention.  All pointers are caller-owned device memory,
+ * 16-byte aligned (RKV_ERR_ARG otherwise); dtype must be bf16.  For the ring, n <= ring_size (RKV_ERR_RING otherwise); for the
  * pool, the table must cover the last position (RKV_ERR_TABLE).  Pool entries outside
  * [0, n_slots) are skipped on the device.  n = 0 does nothing.
  * ------------------------------------------------------------------------------- */
@@ -275,6 +275,7 @@ int32_t ref_layout_to_paged(const void* k_src, const void* v_src, int64_t pos_fi
  * item 1: a pool of 64-token chunks located through a page table; the verify step keeps
  * exactly what greedy decoding by the target would produce).
  *
+ * Rows and stores are 16-byte aligned device memory (RKV_ERR_ARG otherwise).
  * Ring: verify_kv_append_ring writes row i (position pos_first+i) at ring slot
  * (pos_first+i) mod ring_size, 1 <= n <= RKV_MAX_APPEND, n <= ring_size.  Rolling back
  * needs no call: a rejected position is written again by the next block's append before

@@ -135,6 +135,11 @@ void carve(void* ws, const rkv_attn_dims* d, int32_t splits, float** po, float**
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? RKV_OK : RKV_ERR_HIP; }
 
+// The row copies into the chunked stores move 16-byte pieces.
+bool aligned16(const void* a, const void* b, const void* c, const void* d) {
+  return (((uintptr_t)a | (uintptr_t)b | (uintptr_t)c | (uintptr_t)d) & 15) == 0;
+}
+
 int32_t run_chunk_attn(ChunkAttnArgs& a, const rkv_attn_dims* d, void* ws, float* out,
                        float* lse, hipStream_t st) {
   if (a.cps > rkv::kMaxSplitChunks) return RKV_ERR_SHAPE;
@@ -622,6 +627,7 @@ int32_t ref_layout_to_ring(const void* k_src, const void* v_src, int64_t pos_fir
   if (dtype != RKV_BF16) return RKV_ERR_DTYPE;
   if (n_kv_heads < 1 || (head_dim != 64 && head_dim != 128)) return RKV_ERR_SHAPE;
   if (pos_first < 0 || n < 0) return RKV_ERR_ARG;
+  if (!aligned16(k_src, v_src, k_ring, v_ring)) return RKV_ERR_ARG;
   if (ring_size < kChunk || ring_size % kChunk != 0 || n > ring_size) return RKV_ERR_RING;
   rkv::ScatterArgs a{};
   a.k_src = static_cast<const uint16_t*>(k_src);
@@ -649,6 +655,7 @@ int32_t ref_layout_to_paged(const void* k_src, const void* v_src, int64_t pos_fi
   if (dtype != RKV_BF16) return RKV_ERR_DTYPE;
   if (n_kv_heads < 1 || (head_dim != 64 && head_dim != 128)) return RKV_ERR_SHAPE;
   if (pos_first < 0 || n < 0) return RKV_ERR_ARG;
+  if (!aligned16(k_src, v_src, k_pool, v_pool)) return RKV_ERR_ARG;
   if (chunk_size != kChunk || n_slots < 1) return RKV_ERR_TABLE;
   if (n > 0 && (pos_first + n - 1) / kChunk >= n_table) return RKV_ERR_TABLE;
   rkv::ScatterArgs a{};
@@ -676,6 +683,7 @@ int32_t verify_kv_append_ring(const void* k_new, const void* v_new, int32_t n,
     return RKV_ERR_NULL;
   if (n_kv_heads < 1 || (head_dim != 64 && head_dim != 128)) return RKV_ERR_SHAPE;
   if (n < 1 || n > RKV_MAX_APPEND || pos_first < 0) return RKV_ERR_ARG;
+  if (!aligned16(k_new, v_new, k_ring, v_ring)) return RKV_ERR_ARG;
   if (ring_size < kChunk || ring_size % kChunk != 0 || n > ring_size) return RKV_ERR_RING;
   rkv::ScatterArgs a{};
   a.k_src = static_cast<const uint16_t*>(k_new);
@@ -701,6 +709,7 @@ int32_t verify_kv_append_ring_dev(const void* k_new, const void* v_new, int32_t 
     return RKV_ERR_NULL;
   if (n_kv_heads < 1 || (head_dim != 64 && head_dim != 128)) return RKV_ERR_SHAPE;
   if (n < 1 || n > RKV_MAX_APPEND || pos_cap < 0) return RKV_ERR_ARG;
+  if (!aligned16(k_new, v_new, k_ring, v_ring)) return RKV_ERR_ARG;
   if (ring_size < kChunk || ring_size % kChunk != 0 || n > ring_size) return RKV_ERR_RING;
   rkv::ScatterArgs a{};
   a.k_src = static_cast<const uint16_t*>(k_new);
@@ -727,6 +736,7 @@ int32_t verify_kv_append_paged_dev(const void* k_new, const void* v_new, int32_t
     return RKV_ERR_NULL;
   if (n_kv_heads < 1 || (head_dim != 64 && head_dim != 128)) return RKV_ERR_SHAPE;
   if (n < 1 || n > RKV_MAX_APPEND || pos_cap < 0) return RKV_ERR_ARG;
+  if (!aligned16(k_new, v_new, k_pool, v_pool)) return RKV_ERR_ARG;
   if (n_slots < 1 || n_table < 1) return RKV_ERR_TABLE;
   if ((pos_cap + n + kChunk - 1) / kChunk > n_table) return RKV_ERR_TABLE;
   rkv::ScatterArgs a{};
@@ -761,6 +771,7 @@ int32_t verify_kv_append_paged(const void* k_new, const void* v_new, int32_t n,
     return RKV_ERR_NULL;
   if (n_kv_heads < 1 || (head_dim != 64 && head_dim != 128)) return RKV_ERR_SHAPE;
   if (n < 1 || n > RKV_MAX_APPEND || ctx_len < 0) return RKV_ERR_ARG;
+  if (!aligned16(k_new, v_new, k_pool, v_pool)) return RKV_ERR_ARG;
   if (n_slots < 1 || n_table < 1) return RKV_ERR_TABLE;
   const int64_t c0 = (ctx_len + kChunk - 1) / kChunk;
   const int64_t c1 = (ctx_len + n + kChunk - 1) / kChunk;

@@ -109,7 +109,7 @@ static void pager_random(uint32_t seed) {
 }
 
 static void argument_checks() {
-  char dummy[64];
+  alignas(16) char dummy[64];
   void* P = dummy;
   rkv_attn_dims d{16, 16, 4, 128, 0.f, RKV_BF16};
   rkv_attn_dims bad = d;

@@ -150,6 +150,11 @@ def test_layout_helper_checks():
     assert L.ref_layout_to_paged(P, P, 0, 8193, 4, 128, 1, P, P, P, 128, 128, 64, NULL) == ETABLE
     assert L.ref_layout_to_paged(P, P, 0, 10, 4, 96, 1, P, P, P, 128, 128, 64, NULL) == ESHAPE
     assert L.ref_layout_to_paged(NULL, P, 0, 0, 4, 128, 1, P, P, P, 128, 128, 64, NULL) == OK
+    odd = ctypes.c_void_p(0x1008)                 # 8-byte aligned: the row copies move 16 bytes
+    assert L.ref_layout_to_ring(odd, P, 0, 10, 4, 128, 1, P, P, 2048, NULL) == EARG
+    assert L.ref_layout_to_paged(P, P, 0, 10, 4, 128, 1, odd, P, P, 128, 128, 64, NULL) == EARG
+    assert L.verify_kv_append_ring(P, odd, 16, 100, 4, 128, P, P, 2048, NULL) == EARG
+    assert L.verify_kv_append_ring_dev(P, P, 16, P, 100, 4, 128, P, odd, 2048, NULL) == EARG
 
 
 def test_append_checks():
