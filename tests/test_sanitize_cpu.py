@@ -7,10 +7,10 @@ import subprocess
 
 import pytest
 
+from ring_kv_amd.build import SOURCES   # the library's own source list
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HIPCC = "/opt/rocm/bin/hipcc"
-SOURCES = ["abi.hip", "attn_chunked.hip", "attn_prefill.hip", "attn_merge.hip", "attn_contig.hip",
-           "accept.hip", "layout.hip", "paging.hip", "pager.cpp"]
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="ROCm's hipcc is needed")
