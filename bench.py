@@ -20,10 +20,10 @@ call per single-layer workload).
     python bench.py --mode copy     # plain 1-GiB device copies, for HBM counter calibration
     python bench.py --mode kernel   # the dominant kernel alone (10 launches), for counter runs
     python bench.py --mode prefill-kernel   # the prefill kernel alone at 131,072 (3 launches)
-    python bench.py --mode configs  # each single-layer workload and block append called 100
-                                    # times (30 at 256K, for the prefill blocks and for a page-out
-                                    # and page-in of 128 chunks), a cache-evicting read before
-                                    # each, for a kernel trace
+    python bench.py --mode configs  # each single-layer workload and block append (16 and 1,024
+                                    # rows) called 100 times (30 at 256K, for the prefill blocks
+                                    # and for a page-out and page-in of 128 chunks), a
+                                    # cache-evicting read before each, for a kernel trace
     python bench.py --mode traffic --fetch F.csv --write W.csv --copy-fetch CF.csv --copy-write CW.csv
                                     # HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE /
                                     # WRITE_SIZE counter files, scaled by the copy calibration
@@ -508,6 +508,10 @@ def config_calls(torch, rk, synth, probe, n_small, n_large):
     vp = torch.zeros((2048, 4, 128, 64), dtype=torch.bfloat16, device="cuda")
     table = torch.arange(2050, dtype=torch.int32, device="cuda") % 2048
     run(lambda: rk.verify_kv_append_paged(kb, kb, 131064, kp, vp, table, 2048, [2047]), n_small)
+    kb1 = torch.ones((1024, 4, 128), dtype=torch.bfloat16, device="cuda")
+    run(lambda: rk.verify_kv_append_ring(kb1, kb1, 130048, kr, vr), n_small)
+    new16 = list(range(2032, 2048))
+    run(lambda: rk.verify_kv_append_paged(kb1, kb1, 130048, kp, vp, table, 2032, new16), n_small)
     del kp, vp
     torch.cuda.empty_cache()
     # 1,024-token prefill blocks through the pool and the ring
