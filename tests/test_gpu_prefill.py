@@ -61,17 +61,23 @@ def test_prefill_ring_w512():
 
 
 def test_prefill_pool_131k_sampled_rows():
-    """Full size: every row of the block is computed; sampled rows are checked against the
-    oracle as single-token decodes at their own context (the verify/decode equivalence)."""
+    """Full size: every row of the block is computed; a quarter of its rows are checked against
+    the oracle: four runs of 64 consecutive rows (the block's first and last, one across the
+    256-row tile edge at 256, one inside a tile), each as a 64-query block at its own context, and
+    single rows at the other tile edges as single-token decodes at their own context (the
+    verify/decode equivalence)."""
     c, _ = workload("prefill_pool_131k")
     say("prefill_pool_131k: gpu")
     out, lse = run_gpu(c)
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
     p0 = c.ctx_len - c.q_len
-    for i in (0, 1, 255, 256, 511, 777, 1022, 1023):
+    for a in (0, 224, 600, 960):
+        say(f"prefill_pool_131k: oracle rows {a}..{a + 63}")
+        want = oracle.attention_paged(c.q[a:a + 64], c.k_pool, c.v_pool, c.page_table, p0 + a + 64)
+        assert_attn_close((out[a:a + 64], lse[a:a + 64]), want, "bf16", f"131k rows {a}..{a + 63}")
+    for i in (511, 512, 767, 768):
         want = oracle.attention_paged(c.q[i:i + 1], c.k_pool, c.v_pool, c.page_table, p0 + i + 1)
         assert_attn_close((out[i:i + 1], lse[i:i + 1]), want, "bf16", f"131k row {i}")
-
 
 
 @pytest.mark.parametrize("store,q_len,hq,hkv,d", [("paged", 4096, 16, 4, 128),
