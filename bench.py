@@ -216,7 +216,7 @@ class Stack:
         dims = AttnDims(16, 16, 4, 128, 0.0, 1)
         self.ws_paged = torch.empty(max(1, L.verify_attn_paged_workspace_bytes(ctypes.byref(dims), 131072, 64, 0)),
                                     dtype=torch.uint8, device="cuda")
-        self.ws_ring = torch.empty(max(1, L.verify_attn_ring_workspace_bytes(ctypes.byref(dims), 2048, 512, 0)),
+        self.ws_ring = torch.zeros(max(1, L.verify_attn_ring_workspace_bytes(ctypes.byref(dims), 2048, 512, 0)),
                                    dtype=torch.uint8, device="cuda")
         self.ws_acc = torch.zeros(L.verify_accept_workspace_bytes(16, 65536), dtype=torch.uint8, device="cuda")
         self.splits = rk.verify_attn_paged_auto_splits(16, 4, 128, 16, 131072)

@@ -145,7 +145,17 @@ int32_t decode_attn_ref_layout(const rkv_attn_dims* dims, const void* q, const v
  * rows per KV head is not split, its row tiles fill the chip) whose partials a
  * log-sum-exp merge combines.
  * One range spans at most 2^22 chunks (RKV_ERR_SHAPE otherwise).
+ * Workspace (caller-owned device memory, needed when the span is split): a workspace of at
+ * least verify_attn_ring_workspace_bytes() bytes starts with RKV_RING_COUNTER_BYTES of
+ * counters, which must be zero before the workspace's first use and which every call leaves
+ * zero; with them the call merges the partials inside its one launch where it can (the
+ * workgroups of each KV head and row tile, all on one XCD, wait for each other's partials and
+ * each merges a share of the tile's rows; used when the grid fits one workgroup per compute
+ * unit).  Calls that share a workspace must not overlap, and the counters must not be written
+ * by anything else.  A smaller workspace that still holds the call's partials works without
+ * counters: the partials are merged by a second launch, with the same result bits.
  * ------------------------------------------------------------------------------- */
+#define RKV_RING_COUNTER_BYTES 8192
 size_t verify_attn_ring_workspace_bytes(const rkv_attn_dims* dims, int32_t ring_size,
                                         int32_t window, int32_t num_splits);
 int32_t verify_attn_ring(const rkv_attn_dims* dims, const void* q, const void* k_ring,

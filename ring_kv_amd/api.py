@@ -60,7 +60,9 @@ def _dims(q: torch.Tensor, n_kv_heads: int, scale: float) -> AttnDims:
     return AttnDims(q_len, hq, n_kv_heads, d, float(scale), dt)
 
 
-def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor], zero: bool = False):
+    """The caller's workspace (checked), or a new one of nbytes; zero: a new one starts zeroed (a
+    ring call's workspace begins with counters that must be zero before its first use)."""
     if nbytes == 0:
         return None, 0
     if ws is not None:
@@ -69,7 +71,8 @@ def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
         if ws.numel() * ws.element_size() < nbytes:
             raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, need {nbytes}")
         return ws, ws.numel() * ws.element_size()
-    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+    make = torch.zeros if zero else torch.empty
+    return make(nbytes, dtype=torch.uint8, device=device), nbytes
 
 
 def _outputs(q_len: int, hq: int, d: int, device, out, lse, want_lse):
@@ -189,7 +192,7 @@ def verify_attn_ring(q, k_ring, v_ring, pos0: int, window: int, *, num_splits: i
     dims = _dims(q, hkv, scale)
     L = lib()
     ws, wsb = _workspace(L.verify_attn_ring_workspace_bytes(ctypes.byref(dims), ring_size, window,
-                                                            num_splits), dev, workspace)
+                                                            num_splits), dev, workspace, zero=True)
     check("verify_attn_ring", L.verify_attn_ring(
         ctypes.byref(dims), _ptr(q), _ptr(k_ring), _ptr(v_ring), pos0, pos0 % ring_size,
         ring_size, window, num_splits, _ptr(ws), wsb, _ptr(out), _ptr(lse), _stream(stream, dev)))
@@ -474,7 +477,7 @@ def verify_attn_ring_dev(q, k_ring, v_ring, d_pos, pos_cap: int, window: int, *,
     dims = _dims(q, hkv, scale)
     L = lib()
     ws, wsb = _workspace(L.verify_attn_ring_workspace_bytes(ctypes.byref(dims), ring_size, window,
-                                                            num_splits), dev, workspace)
+                                                            num_splits), dev, workspace, zero=True)
     check("verify_attn_ring_dev", L.verify_attn_ring_dev(
         ctypes.byref(dims), _ptr(q), _ptr(k_ring), _ptr(v_ring), _ptr(d_pos), pos_cap, ring_size,
         window, num_splits, _ptr(ws), wsb, _ptr(out), _ptr(lse), _stream(stream, dev)))

@@ -140,16 +140,20 @@ bool aligned16(const void* a, const void* b, const void* c, const void* d) {
   return (((uintptr_t)a | (uintptr_t)b | (uintptr_t)c | (uintptr_t)d) & 15) == 0;
 }
 
-int32_t run_chunk_attn(ChunkAttnArgs& a, const rkv_attn_dims* d, void* ws, float* out,
-                       float* lse, hipStream_t st) {
+// ws: where the partials go; tickets: the counters of the one-launch ring layer (nullptr: the
+// partials are merged by a second launch)
+int32_t run_chunk_attn(ChunkAttnArgs& a, const rkv_attn_dims* d, void* ws, int32_t* tickets,
+                       float* out, float* lse, hipStream_t st) {
   if (a.cps > rkv::kMaxSplitChunks) return RKV_ERR_SHAPE;
   a.out = out;
   a.lse = lse;
   a.part_o = a.part_lse = nullptr;
+  a.tickets = tickets;
   a.fill_wgs = rkv::device_cu_count();
   if (a.num_splits > 1) carve(ws, d, a.num_splits, &a.part_o, &a.part_lse);
-  hipError_t e = rkv::launch_chunk_attn(a, st);
-  if (e != hipSuccess || a.num_splits == 1) return hip_status(e);
+  bool merged = false;
+  hipError_t e = rkv::launch_chunk_attn(a, st, &merged);
+  if (e != hipSuccess || a.num_splits == 1 || merged) return hip_status(e);
   rkv::MergeArgs m{a.part_o, a.part_lse, out, lse, a.q_len, a.G, a.n_q_heads, a.n_kv_heads,
                    a.head_dim, a.num_splits};
   return hip_status(rkv::launch_merge(m, st));
@@ -304,13 +308,38 @@ static int64_t ring_max_chunks(const rkv_attn_dims* d, int32_t window) {
   return (span + kChunk - 2) / kChunk + 1;
 }
 
-size_t verify_attn_ring_workspace_bytes(const rkv_attn_dims* dims, int32_t ring_size,
-                                        int32_t window, int32_t num_splits) {
-  if (check_dims(dims) != RKV_OK || window < 1 || num_splits < 0 || ring_size < kChunk) return 0;
+// A ring call's workspace: kTicketBytes of counters (zero before the workspace's first use,
+// left zero by every call), then the partials of the widest span's split layout.
+static size_t ring_workspace_full(const rkv_attn_dims* dims, int32_t window, int32_t num_splits) {
   int32_t s, cps;
   choose_splits(ring_max_chunks(dims, window), auto_split_target(dims, kRing), num_splits, &s,
                 &cps);
-  return partial_bytes(dims, s);
+  return s > 1 ? rkv::kTicketBytes + partial_bytes(dims, s) : 0;
+}
+
+// Where a ring call's partials and counters go.  A workspace of the full size holds the counters
+// first and the partials after them (one launch where the kernel supports it); a smaller one
+// that still holds this call's partials gets them at its start and no counters (the partials
+// are merged by a second launch).
+static int32_t ring_workspace(const rkv_attn_dims* dims, int32_t window, int32_t num_splits,
+                              int32_t s, void* ws, size_t bytes, void** part_ws,
+                              int32_t** tickets) {
+  *part_ws = ws;
+  *tickets = nullptr;
+  if (s <= 1) return RKV_OK;
+  if (ws == nullptr || bytes < partial_bytes(dims, s)) return RKV_ERR_WORKSPACE;
+  const size_t full = ring_workspace_full(dims, window, num_splits);
+  if (full > 0 && bytes >= full) {
+    *tickets = static_cast<int32_t*>(ws);
+    *part_ws = static_cast<char*>(ws) + rkv::kTicketBytes;
+  }
+  return RKV_OK;
+}
+
+size_t verify_attn_ring_workspace_bytes(const rkv_attn_dims* dims, int32_t ring_size,
+                                        int32_t window, int32_t num_splits) {
+  if (check_dims(dims) != RKV_OK || window < 1 || num_splits < 0 || ring_size < kChunk) return 0;
+  return ring_workspace_full(dims, window, num_splits);
 }
 
 int32_t verify_attn_ring(const rkv_attn_dims* dims, const void* q, const void* k_ring,
@@ -327,8 +356,10 @@ int32_t verify_attn_ring(const rkv_attn_dims* dims, const void* q, const void* k
   int32_t s, cps;
   split_within(n_chunks, ring_max_chunks(dims, window), auto_split_target(dims, kRing),
                num_splits, &s, &cps);
-  if (s > 1 && (workspace == nullptr || workspace_bytes < partial_bytes(dims, s)))
-    return RKV_ERR_WORKSPACE;
+  void* part_ws;
+  int32_t* tickets;
+  st = ring_workspace(dims, window, num_splits, s, workspace, workspace_bytes, &part_ws, &tickets);
+  if (st != RKV_OK) return st;
   ChunkAttnArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k_ring);
@@ -350,7 +381,7 @@ int32_t verify_attn_ring(const rkv_attn_dims* dims, const void* q, const void* k
   a.cps = cps;
   a.num_splits = s;
   a.scale_log2 = scale_log2(dims);
-  return run_chunk_attn(a, dims, workspace, out, lse, static_cast<hipStream_t>(stream));
+  return run_chunk_attn(a, dims, part_ws, tickets, out, lse, static_cast<hipStream_t>(stream));
 }
 
 // ---- paged pool --------------------------------------------------------------------------
@@ -391,7 +422,7 @@ int32_t verify_attn_paged(const rkv_attn_dims* dims, const void* q, const void* 
   if (a.num_splits > 1 &&
       (workspace == nullptr || workspace_bytes < partial_bytes(dims, a.num_splits)))
     return RKV_ERR_WORKSPACE;
-  return run_chunk_attn(a, dims, workspace, out, lse, static_cast<hipStream_t>(stream));
+  return run_chunk_attn(a, dims, workspace, nullptr, out, lse, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"
@@ -441,7 +472,7 @@ int32_t verify_attn_paged_noalloc(const rkv_attn_dims* dims, const void* q, cons
     return RKV_ERR_WORKSPACE;
   void* ws = nullptr;
   if (a.num_splits > 1 && (ws = scratch_address()) == nullptr) return RKV_ERR_HIP;
-  return run_chunk_attn(a, dims, ws, out, lse, static_cast<hipStream_t>(stream));
+  return run_chunk_attn(a, dims, ws, nullptr, out, lse, static_cast<hipStream_t>(stream));
 }
 
 int32_t verify_attn_paged_resident(const rkv_attn_dims* dims, const void* q,
@@ -490,7 +521,8 @@ int32_t verify_attn_paged_partial(const rkv_attn_dims* dims, const void* q,
   a.part_o = part_out;     // partial layout even for one split
   a.part_lse = part_lse;
   a.fill_wgs = rkv::device_cu_count();
-  return hip_status(rkv::launch_chunk_attn(a, static_cast<hipStream_t>(stream)));
+  bool merged = false;
+  return hip_status(rkv::launch_chunk_attn(a, static_cast<hipStream_t>(stream), &merged));
 }
 
 // ---- one captured step replayed across decode steps: the block position on the device ----
@@ -509,8 +541,10 @@ int32_t verify_attn_ring_dev(const rkv_attn_dims* dims, const void* q, const voi
   const int64_t n_max = ring_max_chunks(dims, window);
   int32_t s, cps;
   choose_splits(n_max, auto_split_target(dims, kRing), num_splits, &s, &cps);
-  if (s > 1 && (workspace == nullptr || workspace_bytes < partial_bytes(dims, s)))
-    return RKV_ERR_WORKSPACE;
+  void* part_ws;
+  int32_t* tickets;
+  st = ring_workspace(dims, window, num_splits, s, workspace, workspace_bytes, &part_ws, &tickets);
+  if (st != RKV_OK) return st;
   ChunkAttnArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k_ring);
@@ -530,7 +564,7 @@ int32_t verify_attn_ring_dev(const rkv_attn_dims* dims, const void* q, const voi
   a.d_pos = d_pos;
   a.pos_cap = pos_cap;
   a.ring_size = ring_size;
-  return run_chunk_attn(a, dims, workspace, out, lse, static_cast<hipStream_t>(stream));
+  return run_chunk_attn(a, dims, part_ws, tickets, out, lse, static_cast<hipStream_t>(stream));
 }
 
 int32_t verify_attn_paged_dev(const rkv_attn_dims* dims, const void* q, const void* k_pool,
@@ -556,7 +590,7 @@ int32_t verify_attn_paged_dev(const rkv_attn_dims* dims, const void* q, const vo
     return RKV_ERR_WORKSPACE;
   a.d_pos = d_pos;
   a.pos_cap = pos_cap;
-  return run_chunk_attn(a, dims, workspace, out, lse, static_cast<hipStream_t>(stream));
+  return run_chunk_attn(a, dims, workspace, nullptr, out, lse, static_cast<hipStream_t>(stream));
 }
 
 int32_t attn_merge_partials(const rkv_attn_dims* dims, int32_t num_splits,

@@ -18,6 +18,11 @@
 // of 16-key tiles the key order is permuted (sigma below) so that each lane's 8 P values
 // are 8 consecutive keys, which the dimension-major V chunk supplies as one 16-byte read.
 //
+// A ring layer can run as one launch (FUSE): the split workgroups of each (KV head, row tile)
+// are placed on one XCD, store their partials, wait for each other through a counter in the
+// workspace, and each merges a share of the tile's rows from that XCD's L2; otherwise a second
+// launch merges the partials (attn_merge.hip), with the same bits.
+//
 // Memory path: K and V chunks stream from HBM with 16-byte loads (a wave reads 1 KiB contiguous
 // per instruction) two chunks ahead of the compute, staged in registers and written into two
 // XOR-swizzled LDS tiles that all waves read.  (The direct HBM-to-LDS loads of gfx950 were
@@ -93,6 +98,102 @@ struct Tile {
   }
 };
 
+// hardware register XCC_ID (id 20, all 32 bits): the XCD the wave runs on
+constexpr int kHwRegXccId = 20 | (31 << 11);
+
+// Counter word of a (KV head, row tile) group in the one-launch ring layer: arrivals (bits
+// 0..4), departures (bits 5..9), the sum of the arrivals' XCD ids (bits 10..17) and of their
+// squares (bits 18..29).  Equal sums of ids and of squared ids (S times one id and S times its
+// square) force every id to be that one.
+constexpr int kArrive = 1;
+constexpr int kDepart = 1 << 5;
+constexpr int kSpinLimit = 1 << 17;    // polls before a workgroup gives up (NaN rows)
+
+// This workgroup's share of the merge of its (KV head g, row tile) group's partials, once every
+// workgroup of the group has stored its own: local rows s, s + S, s + 2S, ... of the tile.  The
+// arithmetic is merge_kernel's (the same weights, the same split groups summed in the same
+// order), so both paths give the same bits.  Each pass takes RPP rows, D/4 threads per row, each
+// owning four output dimensions, so a wave instruction reads whole 4*D-byte partial rows; the
+// split weights of a row are computed once (one exponential per thread) and shared through
+// LDS.  Loads miss the L1 (cache policy sc0) and find the partials in the XCD's L2.  bad: write
+// NaN instead (a workgroup of the group ran on another XCD, or never arrived).
+template <int D, int NT, int ROWS>
+__device__ __forceinline__ void merge_share(const ChunkAttnArgs& a, int g, int row0, int s,
+                                            bool bad) {
+  constexpr int PR = D / 4;                       // four-element columns per row
+  constexpr int RPP = NT / PR;                    // rows per pass
+  constexpr int SG = merge_groups<D>();
+  static_assert(NT % PR == 0 && PR >= kFuseMaxSplits && kFuseMaxSplits % 4 == 0, "merge layout");
+  __shared__ __attribute__((aligned(16))) float w_sh[RPP][kFuseMaxSplits];
+  const int rows = a.q_len * a.G;
+  const int S = a.num_splits;
+  const int tid = threadIdx.x;
+  const int col = tid % PR;
+  const int slot = tid / PR;
+  const uint32_t prows = (uint32_t)(a.n_kv_heads * S * rows);
+  const __amdgpu_buffer_rsrc_t po =
+      __builtin_amdgcn_make_buffer_rsrc(a.part_o, 0, prows * D * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t pl =
+      __builtin_amdgcn_make_buffer_rsrc(a.part_lse, 0, prows * 4, 0x00020000);
+  const int mine = (ROWS - s + S - 1) / S;        // local rows of this workgroup
+  const float nan = __builtin_nanf("");
+  for (int q0 = 0; q0 < mine; q0 += RPP) {
+    const int lr = s + S * (q0 + slot);           // local row of this thread
+    const int r = min(row0 + lr, rows - 1);       // clamped: every load is in range
+    auto prow_of = [&](int k) __attribute__((always_inline)) {
+      return (uint32_t)((g * S + min(k, S - 1)) * rows + r);
+    };
+    float lv[kFuseMaxSplits];
+    f32x4 ov[kFuseMaxSplits];
+#pragma unroll
+    for (int k = 0; k < kFuseMaxSplits; ++k) {
+      lv[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pl, prow_of(k) * 4, 0, 1));
+      ov[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            po, (prow_of(k) * D + 4 * col) * 4, 0, 1));
+    }
+    const float l_col = col < kFuseMaxSplits
+        ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pl, prow_of(col) * 4, 0, 1))
+        : 0.f;
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kFuseMaxSplits; ++k)
+      if (k < S) M = fmaxf(M, lv[k]);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    if (col < kFuseMaxSplits) w_sh[slot][col] = col < S ? merge_weight(l_col, Mu) : 0.f;
+    lds_barrier();
+    float wv[kFuseMaxSplits];
+#pragma unroll
+    for (int k4 = 0; k4 < kFuseMaxSplits / 4; ++k4) {
+      const f32x4 w4 = *reinterpret_cast<const f32x4*>(&w_sh[slot][4 * k4]);
+      wv[4 * k4] = w4[0]; wv[4 * k4 + 1] = w4[1]; wv[4 * k4 + 2] = w4[2]; wv[4 * k4 + 3] = w4[3];
+    }
+    if (q0 + slot < mine && row0 + lr < rows) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      float Lt = 0.f;
+#pragma unroll
+      for (int sg = 0; sg < SG; ++sg) {
+        f32x4 acc_g = f32x4{0.f, 0.f, 0.f, 0.f};
+        float L_g = 0.f;
+        // splits k >= S weigh exactly 0 here: adding o * 0 = +-0 to a sum that is never -0 (it
+        // starts at +0, and a sum that cancels to zero is +0) leaves its bits as merge_kernel's,
+        // which skips them; a NaN partial still makes the row NaN
+#pragma unroll
+        for (int k = sg; k < kFuseMaxSplits; k += SG) merge_add(acc_g, L_g, ov[k], wv[k]);
+        Lt += L_g;
+        if (sg == 0) acc = acc_g;
+        else acc += acc_g;
+      }
+      const int qi = r / a.G;
+      const int h = g * a.G + r % a.G;
+      *reinterpret_cast<f32x4*>(a.out + ((int64_t)qi * a.n_q_heads + h) * D + 4 * col) =
+          bad ? f32x4{nan, nan, nan, nan} : merge_out(acc, Lt);
+      if (a.lse != nullptr && col == 0)
+        a.lse[(int64_t)qi * a.n_q_heads + h] = bad ? nan : merge_lse(M, Lt);
+    }
+    lds_barrier();                                // w_sh is rewritten by the next pass
+  }
+}
+
 // Template parameters:
 //   NRG    row groups: wave (rg, kh) owns rows 16*rg .. 16*rg+15 of the KV head's rows
 //   KS     key halves: with KS = 2 each chunk's 64 keys are split between two waves per row
@@ -100,7 +201,9 @@ struct Tile {
 //          states merge through LDS at the end.  Two waves per SIMD, each with half the
 //          dependent work per chunk.
 //   PAGED  slots come from the page table; otherwise the store is a ring (slot = c mod n_slots)
-template <int D, int NRG, int KS, bool PAGED>
+//   FUSE   the one-launch layer: the workgroups of each (KV head, row tile) merge the tile's
+//          partials once all are stored (see merge_share above); the grid is one-dimensional
+template <int D, int NRG, int KS, bool PAGED, bool FUSE>
 __global__ __launch_bounds__(NRG * KS * 64)
 void chunk_attn_kernel(ChunkAttnArgs a) {
   using T = Tile<D>;
@@ -123,6 +226,7 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[NLDS][T::elems];
   __shared__ int pt_lds[kPtCap];
   __shared__ int wave_flag[NW];   // per wave: a table entry of the split is out of range
+  __shared__ int merge_flag;      // FUSE: 1 the group's partials are all stored, 2 write NaN
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -132,9 +236,23 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
   const int ln = lane & 15;
   const int lq = lane >> 4;
 
-  const int b = xcd_block(blockIdx.x, gridDim.x);
-  const int g = b % a.n_kv_heads;
-  const int s = b / a.n_kv_heads;
+  int g, s, tile, grp = 0;
+  if constexpr (FUSE) {
+    // The S workgroups of group grp = (KV head, row tile) are blocks x, x + 8, x + 16, ... of
+    // one residue x mod 8: the dispatcher deals blocks round-robin over the 8 XCDs, so a group
+    // runs on one XCD and shares its L2.
+    const int per_xcd = gridDim.x / kXcds;
+    const int j = blockIdx.x / kXcds;
+    grp = (blockIdx.x % kXcds) * (per_xcd / a.num_splits) + j / a.num_splits;
+    s = j % a.num_splits;
+    g = grp % a.n_kv_heads;
+    tile = grp / a.n_kv_heads;
+  } else {
+    const int b = xcd_block(blockIdx.x, gridDim.x);
+    g = b % a.n_kv_heads;
+    s = b / a.n_kv_heads;
+    tile = blockIdx.y;
+  }
   const int G = a.G;
   const int rows = a.q_len * G;
 
@@ -166,8 +284,8 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
   const int64_t c_end = c_first + n_chunks;
   const int nloc = (int)imax64(0, imin64((int64_t)a.cps, c_end - c_lo));
 
-  // ---- this lane's query row (row tile blockIdx.y holds rows 16*NRG*y ..) ----------------
-  const int row0 = blockIdx.y * (NRG * 16);
+  // ---- this lane's query row (row tile y holds rows 16*NRG*y ..) ---------------------------
+  const int row0 = tile * (NRG * 16);
   const int r = row0 + rg * 16 + ln;
   const bool row_ok = r < rows;
   const int qi = row_ok ? r / G : 0;
@@ -590,8 +708,10 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
       }
     }
     lds_barrier();
-    if (kh == 1) return;
-    if (wave_active) {
+    if constexpr (!FUSE) {
+      if (kh == 1) return;
+    }
+    if (kh == 0 && wave_active) {
       const float m1 = xm[rg * 16 + ln];
       const float l1 = xl[rg * 16 + ln];
       const float M = fmaxf(m_run, m1);
@@ -608,34 +728,86 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
       m_run = M;
     }
   }
-  if (!wave_active || !row_ok) return;
-  // a device position out of range: every output of the call is NaN
-  const float inv = pos_bad ? __builtin_nanf("") : (l > 0.f ? 1.f / l : 0.f);
-  const float lse_nat = pos_bad ? __builtin_nanf("")
-                                : (lfr > 0.f ? (m_run + log2f(lfr)) * kLn2 : -INFINITY);
-  float* dst;
-  if (a.part_o == nullptr) {
-    dst = a.out + ((int64_t)qi * a.n_q_heads + hq) * D;
-    if (a.lse != nullptr && lq == 0) a.lse[(int64_t)qi * a.n_q_heads + hq] = lse_nat;
-  } else {
-    const int64_t prow = ((int64_t)g * a.num_splits + s) * rows + r;
-    dst = a.part_o + prow * D;
-    if (lq == 0) a.part_lse[prow] = lse_nat;
-  }
+  auto store_rows = [&]() __attribute__((always_inline)) {
+    // a device position out of range: every output of the call is NaN
+    const float inv = pos_bad ? __builtin_nanf("") : (l > 0.f ? 1.f / l : 0.f);
+    const float lse_nat = pos_bad ? __builtin_nanf("")
+                                  : (lfr > 0.f ? (m_run + log2f(lfr)) * kLn2 : -INFINITY);
+    float* dst;
+    if (a.part_o == nullptr) {
+      dst = a.out + ((int64_t)qi * a.n_q_heads + hq) * D;
+      if (a.lse != nullptr && lq == 0) a.lse[(int64_t)qi * a.n_q_heads + hq] = lse_nat;
+    } else {
+      const int64_t prow = ((int64_t)g * a.num_splits + s) * rows + r;
+      dst = a.part_o + prow * D;
+      if (lq == 0) a.part_lse[prow] = lse_nat;
+    }
 #pragma unroll
-  for (int t = 0; t < TMD; ++t) {
-    f32x4 o = oacc[t] * inv;
-    *reinterpret_cast<f32x4*>(dst + 16 * t + 4 * lq) = o;
+    for (int t = 0; t < TMD; ++t) {
+      f32x4 o = oacc[t] * inv;
+      *reinterpret_cast<f32x4*>(dst + 16 * t + 4 * lq) = o;
+    }
+  };
+  if constexpr (!FUSE) {
+    if (!wave_active || !row_ok) return;
+    store_rows();
+  } else {
+    if ((KS == 1 || kh == 0) && wave_active && row_ok) store_rows();
+    // ---- the group merges its partials once all of them are stored ---------------------------
+    // A workgroup's stores reach the XCD's L2 (the L1 writes through) once acknowledged; its
+    // arrival follows every thread's acknowledgement.  Every workgroup of the group then waits
+    // (a bounded poll) for the group's S arrivals and merges its share of the tile's rows.  The
+    // group's workgroups are all resident at once (the launch is used only when its grid fits
+    // one workgroup per compute unit), so the wait ends when the slowest of them arrives.  The
+    // last to leave resets the counter to zero.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int* const ticket = a.tickets + grp * (kTicketStride / 4);
+    const int S = a.num_splits;
+    if (tid == 0) {
+      const int x = (int)((uint32_t)__builtin_amdgcn_s_getreg(kHwRegXccId) & 15u);
+      const int arrive = kArrive + (x << 10) + ((x * x) << 18);
+      int v = __hip_atomic_fetch_add(ticket, arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) +
+              arrive;
+      for (int polls = 0; (v & 31) < S && polls < kSpinLimit; ++polls) {
+        __builtin_amdgcn_s_sleep(2);
+        v = __hip_atomic_fetch_add(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      const bool all_here = (v & 31) == S && ((v >> 10) & 255) == S * x &&
+                            ((v >> 18) & 4095) == S * x * x;
+      merge_flag = all_here ? 1 : 2;
+    }
+    __syncthreads();
+    const int f = merge_flag;
+    int dep = 0;
+    if (tid == 0)     // leave; the returned count is looked at after the merge
+      dep = __hip_atomic_fetch_add(ticket, kDepart, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    merge_share<D, NRG * KS * 64, NRG * 16>(a, g, row0, s, f == 2);
+    if (tid == 0 && ((dep >> 5) & 31) == S - 1)
+      __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
 template <int D, int NRG, int KS>
-hipError_t launch_t(const ChunkAttnArgs& a, hipStream_t stream) {
+hipError_t launch_t(const ChunkAttnArgs& a, hipStream_t stream, bool* merged) {
   const int rows = a.q_len * a.G;
-  const dim3 blocks(a.n_kv_heads * a.num_splits, (rows + NRG * 16 - 1) / (NRG * 16));
+  const int tiles = (rows + NRG * 16 - 1) / (NRG * 16);
+  const dim3 blocks(a.n_kv_heads * a.num_splits, tiles);
   const dim3 threads(NRG * KS * 64);
-  if (a.pt != nullptr) return launch_kernel(chunk_attn_kernel<D, NRG, KS, true>, blocks, threads, a, stream);
-  return launch_kernel(chunk_attn_kernel<D, NRG, KS, false>, blocks, threads, a, stream);
+  if (a.pt != nullptr)
+    return launch_kernel(chunk_attn_kernel<D, NRG, KS, true, false>, blocks, threads, a, stream);
+  // the one-launch ring layer: counters given, few enough splits for the merge's registers,
+  // (KV head, row tile) groups that divide evenly over the XCDs, and a grid that fits one
+  // workgroup per compute unit (every workgroup of a group is resident while the others wait)
+  const int64_t groups = (int64_t)a.n_kv_heads * tiles;
+  if (a.tickets != nullptr && a.part_o != nullptr && a.num_splits > 1 &&
+      a.num_splits <= kFuseMaxSplits && groups % kXcds == 0 &&
+      groups * kTicketStride <= (int64_t)kTicketBytes && groups * a.num_splits <= a.fill_wgs) {
+    *merged = true;
+    return launch_kernel(chunk_attn_kernel<D, NRG, KS, false, true>,
+                         dim3((unsigned)(groups * a.num_splits)), threads, a, stream);
+  }
+  return launch_kernel(chunk_attn_kernel<D, NRG, KS, false, false>, blocks, threads, a, stream);
 }
 
 // Tiles of 64 rows (blockIdx.y), two waves per row group (key halves).  Tiles of one split
@@ -648,20 +820,21 @@ hipError_t launch_t(const ChunkAttnArgs& a, hipStream_t stream) {
 // first time from cache.  A grid of 132 workgroups keeps 64 rows (264 would take two rounds),
 // and the long contexts keep them too, their 256 workgroups already filling the chip.
 template <int D>
-hipError_t launch_d(const ChunkAttnArgs& a, hipStream_t stream) {
+hipError_t launch_d(const ChunkAttnArgs& a, hipStream_t stream, bool* merged) {
   const int rows = a.q_len * a.G;
   const int64_t wgs = (int64_t)a.n_kv_heads * a.num_splits * ((rows + 63) / 64);
-  if (4 * wgs <= a.fill_wgs) return launch_t<D, 1, 2>(a, stream);
-  if (2 * wgs <= a.fill_wgs) return launch_t<D, 2, 2>(a, stream);
-  return launch_t<D, 4, 2>(a, stream);
+  if (4 * wgs <= a.fill_wgs) return launch_t<D, 1, 2>(a, stream, merged);
+  if (2 * wgs <= a.fill_wgs) return launch_t<D, 2, 2>(a, stream, merged);
+  return launch_t<D, 4, 2>(a, stream, merged);
 }
 
 }  // namespace
 
-hipError_t launch_chunk_attn(const ChunkAttnArgs& a, hipStream_t stream) {
+hipError_t launch_chunk_attn(const ChunkAttnArgs& a, hipStream_t stream, bool* merged) {
+  *merged = false;
   if (a.q_len * a.G > kVerifyMaxRows) return launch_prefill_attn(a, stream);
-  if (a.head_dim == 128) return launch_d<128>(a, stream);
-  return launch_d<64>(a, stream);
+  if (a.head_dim == 128) return launch_d<128>(a, stream, merged);
+  return launch_d<64>(a, stream, merged);
 }
 
 }  // namespace rkv

@@ -34,6 +34,7 @@ template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   constexpr int PR = D / 4;                 // float4 per row
   constexpr int SG = kMergeThreads / PR;    // split groups
+  static_assert(SG == merge_groups<D>(), "the split grouping every merge path shares");
   __shared__ float red[kMergeThreads / 64];
   __shared__ f32x4 xacc[SG][PR];
   __shared__ float xl[SG];
@@ -65,18 +66,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
 #pragma unroll
-  for (int u = 0; u < kPre; ++u) {
-    const int s = sg + SG * u;
-    const float w = (s < S && lv[u] != -INFINITY) ? expf(lv[u] - Mu) : 0.f;
-    acc += ov[u] * w;
-    L += w;
-  }
-  for (int s = sg + SG * kPre; s < S; s += SG) {
-    const float ls = lse[(int64_t)s * rows];
-    const float w = ls != -INFINITY ? expf(ls - Mu) : 0.f;
-    acc += *reinterpret_cast<const f32x4*>(po + s * ostride) * w;
-    L += w;
-  }
+  for (int u = 0; u < kPre; ++u)
+    if (sg + SG * u < S) merge_term(acc, L, ov[u], lv[u], Mu);
+  for (int s = sg + SG * kPre; s < S; s += SG)
+    merge_term(acc, L, *reinterpret_cast<const f32x4*>(po + s * ostride),
+               lse[(int64_t)s * rows], Mu);
   xacc[sg][tid % PR] = acc;
   if (tid % PR == 0) xl[sg] = L;
   __syncthreads();
@@ -89,14 +83,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   const int qi = r / a.G;
   const int h = g * a.G + r % a.G;
   *reinterpret_cast<f32x4*>(a.out + ((int64_t)qi * a.n_q_heads + h) * D + d4) =
-      Lt != 0.f ? acc * (1.f / Lt) : f32x4{0.f, 0.f, 0.f, 0.f};
-  if (a.lse != nullptr && d4 == 0)
-    a.lse[(int64_t)qi * a.n_q_heads + h] = Lt != 0.f ? M + logf(Lt) : -INFINITY;
+      merge_out(acc, Lt);
+  if (a.lse != nullptr && d4 == 0) a.lse[(int64_t)qi * a.n_q_heads + h] = merge_lse(M, Lt);
 }
 
 // Many rows, few splits (a prefill block): D/4 threads per row, each owning four consecutive
-// dimensions and walking the splits in order; no LDS, no barrier, and each row's partials are
-// read as whole 4*D-byte lines.
+// dimensions and walking the splits group by group (merge_kernel's grouping, so the same bits);
+// no LDS, no barrier, and each row's partials are read as whole 4*D-byte lines.
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_rows_kernel(MergeArgs a) {
   constexpr int TPR = D / 4;
@@ -114,20 +107,25 @@ __global__ __launch_bounds__(kMergeThreads) void merge_rows_kernel(MergeArgs a) 
   float M = -INFINITY;
   for (int s = 0; s < S; ++s) M = fmaxf(M, lse[(int64_t)s * rows]);
   const float Mu = M == -INFINITY ? 0.f : M;
+  // the split groups of merge_kernel, one after the other (the same bits)
+  constexpr int SG = merge_groups<D>();
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  float L = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float ls = lse[(int64_t)s * rows];
-    const float w = ls != -INFINITY ? expf(ls - Mu) : 0.f;
-    acc += *reinterpret_cast<const f32x4*>(po + s * ostride) * w;
-    L += w;
+  float Lt = 0.f;
+  for (int sg = 0; sg < SG; ++sg) {
+    f32x4 acc_g = f32x4{0.f, 0.f, 0.f, 0.f};
+    float L_g = 0.f;
+    for (int s = sg; s < S; s += SG)
+      merge_term(acc_g, L_g, *reinterpret_cast<const f32x4*>(po + s * ostride),
+                 lse[(int64_t)s * rows], Mu);
+    Lt += L_g;
+    if (sg == 0) acc = acc_g;
+    else acc += acc_g;
   }
   const int qi = r / a.G;
   const int h = g * a.G + r % a.G;
   *reinterpret_cast<f32x4*>(a.out + ((int64_t)qi * a.n_q_heads + h) * D + d4) =
-      L != 0.f ? acc * (1.f / L) : f32x4{0.f, 0.f, 0.f, 0.f};
-  if (a.lse != nullptr && d4 == 0)
-    a.lse[(int64_t)qi * a.n_q_heads + h] = L != 0.f ? M + logf(L) : -INFINITY;
+      merge_out(acc, Lt);
+  if (a.lse != nullptr && d4 == 0) a.lse[(int64_t)qi * a.n_q_heads + h] = merge_lse(M, Lt);
 }
 
 // rows of all KV heads from which the row-parallel form is used (with at most kRowsMaxSplits)

@@ -51,4 +51,31 @@ __device__ __forceinline__ int xcd_block(int b, int nb) {
   return (nb & 7) ? b : (b & 7) * (nb >> 3) + (b >> 3);
 }
 
+// ---- log-sum-exp merge of split partials ----------------------------------------------------
+// Each output element sums, for each split group k = s mod SG, the group's splits in order of s,
+// then the SG group sums in order of k (SG = 1024 / D: the merge kernel's 256 threads hold D / 4
+// four-element columns per group).  Every merge path here uses this grouping and these helpers,
+// so all of them give the same bits.
+template <int D>
+constexpr int merge_groups() { return 1024 / D; }
+
+// Split s's weight exp(lse_s - Mu) (an lse of -inf, a split that saw no key of the row, weighs
+// 0; a NaN lse weighs NaN and the row comes out NaN), and its term added to the running sums.
+__device__ __forceinline__ float merge_weight(float ls, float Mu) {
+  return ls != -INFINITY ? expf(ls - Mu) : 0.f;
+}
+__device__ __forceinline__ void merge_add(f32x4& acc, float& L, f32x4 o, float w) {
+  acc += o * w;
+  L += w;
+}
+__device__ __forceinline__ void merge_term(f32x4& acc, float& L, f32x4 o, float ls, float Mu) {
+  merge_add(acc, L, o, merge_weight(ls, Mu));
+}
+__device__ __forceinline__ f32x4 merge_out(f32x4 acc, float Lt) {
+  return Lt != 0.f ? acc * (1.f / Lt) : f32x4{0.f, 0.f, 0.f, 0.f};
+}
+__device__ __forceinline__ float merge_lse(float M, float Lt) {
+  return Lt != 0.f ? M + logf(Lt) : -INFINITY;
+}
+
 }  // namespace rkv

@@ -55,13 +55,30 @@ struct ChunkAttnArgs {
   int64_t pos_cap;
   int32_t ring_size;      // positions the ring holds (ring only)
   int32_t fill_wgs;       // workgroups of one round over the device (its compute units)
+  // Counters of the one-launch ring layer (nullptr: the partials are merged by a second
+  // launch): one int per (KV head, row tile), each in a 128-byte line of its own, zero before
+  // the launch and left zero by it.
+  int32_t* tickets;
 };
+
 // Blocks of up to kVerifyMaxRows rows per KV head (a verify block: q_len * G) run the
 // HBM-streaming kernel with 16-, 32- or 64-row tiles (the smallest whose grid fits one round of
 // fill_wgs workgroups, one per compute unit); longer blocks (batched prefill) run the
 // matrix-core kernel with tiles of kPrefillTileRows rows.  launch_chunk_attn picks the kernel.
 constexpr int kVerifyMaxRows = 256;
 constexpr int kPrefillTileRows = 256;
+// The one-launch ring layer: the workgroups of one (KV head, row tile) all run on one XCD; once
+// all of them have stored their partials, each merges a share of the tile's rows, reading the
+// partials from that XCD's L2.  Used for ring splits up to kFuseMaxSplits whose (head, tile)
+// groups divide evenly over the kXcds XCDs and whose grid fits one workgroup per compute unit.
+constexpr int kFuseMaxSplits = 12;
+constexpr int kXcds = 8;
+// Bytes of counters the one-launch ring layer keeps at the start of a ring call's workspace: one
+// int per (KV head, row tile) every kTicketStride bytes (the counters of different groups never
+// share a cache line: every workgroup's add goes to the device-wide coherence point, and adds to
+// one line queue there), for up to 64 groups.
+constexpr size_t kTicketBytes = RKV_RING_COUNTER_BYTES;
+constexpr int kTicketStride = 128;
 // Row tile of the prefill kernel: kPrefillTileRows, or half of it (two waves per row group, one
 // per half of each chunk's keys) when the full tiles would leave most of the chip without a
 // workgroup (fewer than `fill`, the compute units), or a quarter of it (two row groups) where
@@ -74,7 +91,9 @@ inline int prefill_tile_rows(int rows, int n_kv_heads, int num_splits, int fill)
   if (grid(kPrefillTileRows / 4) <= fill) return kPrefillTileRows / 4;
   return kPrefillTileRows / 2;
 }
-hipError_t launch_chunk_attn(const ChunkAttnArgs& a, hipStream_t stream);
+// *merged: true when the launch also merged the partials into out / lse (the one-launch ring
+// layer), so that no merge launch follows.
+hipError_t launch_chunk_attn(const ChunkAttnArgs& a, hipStream_t stream, bool* merged);
 hipError_t launch_prefill_attn(const ChunkAttnArgs& a, hipStream_t stream);
 
 struct MergeArgs {

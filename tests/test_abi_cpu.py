@@ -114,12 +114,14 @@ def test_ring_argument_checks():
     assert ring(window=0) == EARG
     assert ring(pos0=-1, head=0) == EARG
     assert ring(d=dims(dtype=0)) == EDTYPE
-    # 527 positions touch at most 10 chunks: one chunk per split by default, partials
-    # [4][10][64][128] + [4][10][64] floats
-    want = 4 * 10 * 64 * 128 * 4 + 4 * 10 * 64 * 4
+    # 527 positions touch at most 10 chunks: one chunk per split by default; 8,192 bytes of
+    # counters, then partials [4][10][64][128] + [4][10][64] floats
+    part = 4 * 10 * 64 * 128 * 4 + 4 * 10 * 64 * 4
+    want = 8192 + part
     assert L.verify_attn_ring_workspace_bytes(dims(), 2048, 512, 0) == want
     assert L.verify_attn_ring_workspace_bytes(dims(), 2048, 512, 10) == want
     assert ring(ws=NULL) == EWS
+    assert ring(wsb=8192) == EWS                           # room for the counters only
 
 
 def test_contiguous_and_merge_checks():
@@ -255,7 +257,7 @@ def test_device_position_checks():
     assert rd(size=512) == ERING and rd(size=2000) == ERING
     assert rd(d=dims(dtype=0)) == EDTYPE
     assert rd(d=dims(q_len=65)) == ESHAPE                 # 260 rows per KV head: prefill-sized
-    assert rd(ws=NULL) == EWS and rd(wsb=ws_ring - 1) == EWS
+    assert rd(ws=NULL) == EWS and rd(wsb=ws_ring - 8192 - 1) == EWS   # partials do not fit
     cap = 131056
     ws_pool = L.verify_attn_paged_workspace_bytes(dims(), cap + 16, 64, 0)
     pd = lambda d=None, pos=P, cap=cap, n_table=2048, chunk=64, ws=P, wsb=ws_pool: \

@@ -30,7 +30,7 @@ def test_graph_replay_stack_40l_131k_against_oracle():
     dims = AttnDims(16, 16, 4, 128, 0.0, 1)
     ws_p = torch.empty(L.verify_attn_paged_workspace_bytes(ctypes.byref(dims), 131072, 64, 0),
                        dtype=torch.uint8, device="cuda")
-    ws_r = torch.empty(L.verify_attn_ring_workspace_bytes(ctypes.byref(dims), 2048, 512, 0),
+    ws_r = torch.zeros(L.verify_attn_ring_workspace_bytes(ctypes.byref(dims), 2048, 512, 0),
                        dtype=torch.uint8, device="cuda")
     layers, refs = [], []
     acc = None
