@@ -60,9 +60,8 @@ def _dims(q: torch.Tensor, n_kv_heads: int, scale: float) -> AttnDims:
     return AttnDims(q_len, hq, n_kv_heads, d, float(scale), dt)
 
 
-def _workspace(nbytes: int, device, ws: Optional[torch.Tensor], zero: bool = False):
-    """The caller's workspace (checked), or a new one of nbytes; zero: a new one starts zeroed (a
-    ring call's workspace begins with counters that must be zero before its first use)."""
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
+    """The caller's workspace (checked to hold nbytes), or a new one of nbytes."""
     if nbytes == 0:
         return None, 0
     if ws is not None:
@@ -71,8 +70,21 @@ def _workspace(nbytes: int, device, ws: Optional[torch.Tensor], zero: bool = Fal
         if ws.numel() * ws.element_size() < nbytes:
             raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, need {nbytes}")
         return ws, ws.numel() * ws.element_size()
-    make = torch.zeros if zero else torch.empty
-    return make(nbytes, dtype=torch.uint8, device=device), nbytes
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+# Counter bytes at the start of a full-size ring workspace (RKV_RING_COUNTER_BYTES).
+RING_COUNTER_BYTES = 8192
+
+
+def _ring_workspace(full: int, device, ws: Optional[torch.Tensor]):
+    """A ring call's workspace.  full = verify_attn_ring_workspace_bytes(): with it (counters
+    zeroed before first use, which the caller owns) the layer runs as one launch; a workspace of
+    only the partials (full - RING_COUNTER_BYTES) merges in a second launch.  Without a caller
+    workspace a fresh one of the partials' size is used (nothing to zero inside the call)."""
+    if full == 0:
+        return None, 0
+    return _workspace(full - RING_COUNTER_BYTES, device, ws)
 
 
 def _outputs(q_len: int, hq: int, d: int, device, out, lse, want_lse):
@@ -181,7 +193,10 @@ def attn_merge_partials(part_out, part_lse, q_len: int, n_q_heads: int, *, out=N
 def verify_attn_ring(q, k_ring, v_ring, pos0: int, window: int, *, num_splits: int = 0,
                      scale: float = 0.0, out=None, lse=None, want_lse: bool = True,
                      workspace=None, stream=None):
-    """Sliding-window verify block over the position ring (slot = pos mod ring_size)."""
+    """Sliding-window verify block over the position ring (slot = pos mod ring_size).
+    workspace: a persistent uint8 device buffer of verify_attn_ring_workspace_bytes() bytes,
+    zeroed once before its first use, runs the layer as one launch; without one, a fresh buffer
+    of the partials alone is used and a second launch merges them (the same bits)."""
     _form(q, "q", torch.bfloat16, (None, None, None))
     q_len, hq, d = q.shape
     n_chunks, hkv, _ = _chunked(k_ring, v_ring, "k_ring", "v_ring", d)
@@ -191,8 +206,8 @@ def verify_attn_ring(q, k_ring, v_ring, pos0: int, window: int, *, num_splits: i
     ring_size = n_chunks * CHUNK
     dims = _dims(q, hkv, scale)
     L = lib()
-    ws, wsb = _workspace(L.verify_attn_ring_workspace_bytes(ctypes.byref(dims), ring_size, window,
-                                                            num_splits), dev, workspace, zero=True)
+    ws, wsb = _ring_workspace(L.verify_attn_ring_workspace_bytes(ctypes.byref(dims), ring_size,
+                                                                 window, num_splits), dev, workspace)
     check("verify_attn_ring", L.verify_attn_ring(
         ctypes.byref(dims), _ptr(q), _ptr(k_ring), _ptr(v_ring), pos0, pos0 % ring_size,
         ring_size, window, num_splits, _ptr(ws), wsb, _ptr(out), _ptr(lse), _stream(stream, dev)))
@@ -476,8 +491,8 @@ def verify_attn_ring_dev(q, k_ring, v_ring, d_pos, pos_cap: int, window: int, *,
     ring_size = n_chunks * CHUNK
     dims = _dims(q, hkv, scale)
     L = lib()
-    ws, wsb = _workspace(L.verify_attn_ring_workspace_bytes(ctypes.byref(dims), ring_size, window,
-                                                            num_splits), dev, workspace, zero=True)
+    ws, wsb = _ring_workspace(L.verify_attn_ring_workspace_bytes(ctypes.byref(dims), ring_size,
+                                                                 window, num_splits), dev, workspace)
     check("verify_attn_ring_dev", L.verify_attn_ring_dev(
         ctypes.byref(dims), _ptr(q), _ptr(k_ring), _ptr(v_ring), _ptr(d_pos), pos_cap, ring_size,
         window, num_splits, _ptr(ws), wsb, _ptr(out), _ptr(lse), _stream(stream, dev)))

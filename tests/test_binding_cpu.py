@@ -112,3 +112,14 @@ def test_paging_and_resident_checks():
     _fails(lambda: rk.verify_attn_paged_resident(Q, KP, VP, ds, [0, 1, 2, 3], 256), "d_slots")
     _fails(lambda: rk.verify_attn_paged_resident(Q, KP, VP, ds, [0, 1, 2, 3, 4], 320,
                                                  lse=z(16, 16, 1, dtype=f32)), "lse")
+
+
+def test_ring_counter_bytes_match_the_header():
+    """The binding sizes its own ring workspaces without the counters the header reserves at the
+    start of a full-size one (so a fresh workspace needs no zeroing); both must name the same
+    size."""
+    import os
+    import re
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "ring_kv.h")).read()
+    m = re.search(r"#define RKV_RING_COUNTER_BYTES (\d+)", hdr)
+    assert m and int(m.group(1)) == rk.api.RING_COUNTER_BYTES
