@@ -293,6 +293,22 @@ class Stack:
         self.ws_paged_dev = torch.empty(max(1, L.verify_attn_paged_workspace_bytes(
             ctypes.byref(dims), self.pos_cap + 16, 64, 0)), dtype=torch.uint8, device="cuda")
 
+    def decode_step_fused(self):
+        """decode_step with each layer's append inside its attention launch."""
+        rk, cap, dp = self.rk, self.pos_cap, self.d_pos
+        for d in self.layers:
+            if d["kind"] == "ring":
+                rk.verify_attn_ring_append_dev(d["q"], d["k_new"], d["v_new"], d["k"], d["v"], dp,
+                                               cap, d["window"], out=d["out"], lse=d["lse"],
+                                               workspace=self.ws_ring)
+            else:
+                rk.verify_attn_paged_append_dev(d["q"], d["k_new"], d["v_new"], d["k"], d["v"],
+                                                d["pt"], dp, cap, out=d["out"], lse=d["lse"],
+                                                workspace=self.ws_paged_dev)
+        rk.verify_accept(self.logits, self.prop, accept_len=self.acc_len, committed=self.committed,
+                         row_argmax=self.argmax, workspace=self.ws_acc)
+        rk.verify_pos_advance(dp, self.acc_len)
+
     def decode_step(self):
         rk, cap, dp = self.rk, self.pos_cap, self.d_pos
         for d in self.layers:
@@ -1012,25 +1028,32 @@ def main():
             # the decode loop: one captured step (appends + attention + accept + advance, the
             # block position on the device) replayed as the context grows
             n_dec = args.warmup + args.steps + 1
-            st.decode_setup(n_dec)
-            gd = capture(st.decode_step, torch)      # the capture's warm-up run advances once
-            for _ in range(args.warmup):
-                gd.replay()
-            torch.cuda.synchronize()
-            p_start = int(st.d_pos.cpu()[0])
-            dec = per_call_ms(gd.replay, args.steps, torch)
-            p_end = int(st.d_pos.cpu()[0])
-            assert p_end - p_start == args.steps * st.adv and p_end <= st.pos_cap + st.adv
-            dec_bytes = sum(st.decode_kv_bytes(p_start + i * st.adv) for i in range(args.steps))
-            dec_ms = sum(dec) / len(dec)
-            log(f"decode step with appends {dec_ms:.3f} ms")
-            res["step_with_appends"] = {
-                "ms_per_step": round(dec_ms, 4), "step_ms": dist(dec, 4),
-                "kv_gbps": round(dec_bytes / args.steps / (dec_ms * 1e-3) / 1e9, 1),
-                "positions": [p_start, p_end - st.adv], "advance_per_step": st.adv,
-                "note": "one captured graph replayed as the decode loop: per layer the block's "
-                        "16 K/V rows appended at the device-resident position, then attention; "
-                        "the accept and the on-device advance by a + 1"}
+            def decode_loop(step_fn):
+                st.decode_setup(n_dec)
+                gd = capture(step_fn, torch)         # the capture's warm-up run advances once
+                for _ in range(args.warmup):
+                    gd.replay()
+                torch.cuda.synchronize()
+                p_start = int(st.d_pos.cpu()[0])
+                dec = per_call_ms(gd.replay, args.steps, torch)
+                p_end = int(st.d_pos.cpu()[0])
+                assert p_end - p_start == args.steps * st.adv and p_end <= st.pos_cap + st.adv
+                dec_bytes = sum(st.decode_kv_bytes(p_start + i * st.adv)
+                                for i in range(args.steps))
+                dec_ms = sum(dec) / len(dec)
+                del gd
+                return {"ms_per_step": round(dec_ms, 4), "step_ms": dist(dec, 4),
+                        "kv_gbps": round(dec_bytes / args.steps / (dec_ms * 1e-3) / 1e9, 1),
+                        "positions": [p_start, p_end - st.adv], "advance_per_step": st.adv}
+            two = decode_loop(st.decode_step)
+            fused = decode_loop(st.decode_step_fused)
+            log(f"decode step with appends {fused['ms_per_step']:.3f} ms "
+                f"({two['ms_per_step']:.3f} ms with separate append launches)")
+            res["step_with_appends"] = dict(fused, two_calls=two, note=(
+                "one captured graph replayed as the decode loop: per layer the block's 16 K/V "
+                "rows appended at the device-resident position inside the attention launch "
+                "(two_calls: a separate append launch per layer), then the accept and the "
+                "on-device advance by a + 1"))
         del st
         torch.cuda.empty_cache()
 

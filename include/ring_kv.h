@@ -390,6 +390,29 @@ int32_t verify_kv_append_paged_dev(const void* k_new, const void* v_new, int32_t
 int32_t verify_pos_advance(int64_t* d_pos, const int32_t* accept_len, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * The block's append and its attention in one launch (the decode loop's two calls per layer,
+ * verify_kv_append_*_dev then verify_attn_*_dev, as one): k_new, v_new [q_len][Hkv][D] bf16 are
+ * the block's own rows for positions *d_pos .. *d_pos + q_len - 1 (the block's inputs: the last
+ * committed token and the drafts); they are written into their ring or pool slots and attended,
+ * with the same results and the same store contents as the two calls.  Arguments, workspace and
+ * status as verify_attn_ring_dev / verify_attn_paged_dev, plus RKV_ERR_NULL for k_new or v_new
+ * and RKV_ERR_ARG for a row or store pointer that is not 16-byte aligned.  The pool's table
+ * must hold the slots of the block's chunks (reserved before capture); a position outside
+ * [0, pos_cap] writes nothing and gives NaN attention.
+ * ------------------------------------------------------------------------------- */
+int32_t verify_attn_ring_append_dev(const rkv_attn_dims* dims, const void* q, const void* k_new,
+                                    const void* v_new, void* k_ring, void* v_ring,
+                                    const int64_t* d_pos, int64_t pos_cap, int32_t ring_size,
+                                    int32_t window, int32_t num_splits, void* workspace,
+                                    size_t workspace_bytes, float* out, float* lse, void* stream);
+int32_t verify_attn_paged_append_dev(const rkv_attn_dims* dims, const void* q, const void* k_new,
+                                     const void* v_new, void* k_pool, void* v_pool,
+                                     const int32_t* page_table, int32_t n_table, int32_t n_slots,
+                                     int32_t chunk_size, const int64_t* d_pos, int64_t pos_cap,
+                                     int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                     float* out, float* lse, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * Host paging of the pool (lucebox post, "Three optimizations", item 1: only part of the
  * context stays in the GPU pool and 64-token chunks move to host memory and back without any
  * change to their bits; the drafter scores which chunks stay, outside this library).

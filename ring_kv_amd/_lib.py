@@ -76,6 +76,11 @@ _PROTOS = {
                                        _P, c_size_t, _P, _P, _P]),
     "verify_attn_paged_dev": (c_int32, [_DIMS, _P, _P, _P, _P, c_int32, c_int32, c_int32, _P,
                                         c_int64, c_int32, _P, c_size_t, _P, _P, _P]),
+    "verify_attn_ring_append_dev": (c_int32, [_DIMS, _P, _P, _P, _P, _P, _P, c_int64, c_int32,
+                                              c_int32, c_int32, _P, c_size_t, _P, _P, _P]),
+    "verify_attn_paged_append_dev": (c_int32, [_DIMS, _P, _P, _P, _P, _P, _P, c_int32, c_int32,
+                                               c_int32, _P, c_int64, c_int32, _P, c_size_t, _P,
+                                               _P, _P]),
     "verify_kv_append_ring_dev": (c_int32, [_P, _P, c_int32, _P, c_int64, c_int32, c_int32, _P,
                                             _P, c_int32, _P]),
     "verify_kv_append_paged_dev": (c_int32, [_P, _P, c_int32, _P, c_int64, c_int32, c_int32, _P,

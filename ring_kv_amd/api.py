@@ -523,6 +523,66 @@ def verify_attn_paged_dev(q, k_pool, v_pool, page_table, d_pos, pos_cap: int, *,
     return out, lse
 
 
+def _new_rows(q, k_new, v_new, hkv: int):
+    """The block's own rows [q_len][Hkv][D] bf16, one per query row of q."""
+    n, h, d = _rows_pair(k_new, v_new, "k_new", "v_new")
+    if n != q.shape[0] or h != hkv or d != q.shape[2]:
+        raise ValueError(f"k_new/v_new are [{n}][{h}][{d}], need [{q.shape[0]}][{hkv}][{q.shape[2]}]"
+                         " (the block's rows: one per query)")
+
+
+def verify_attn_ring_append_dev(q, k_new, v_new, k_ring, v_ring, d_pos, pos_cap: int,
+                                window: int, *, num_splits: int = 0, scale: float = 0.0, out=None,
+                                lse=None, want_lse: bool = True, workspace=None, stream=None):
+    """verify_kv_append_ring_dev(k_new, v_new, ...) then verify_attn_ring_dev(q, ...) in one
+    launch: the block's rows are written into the ring and attended."""
+    _form(q, "q", torch.bfloat16, (None, None, None))
+    q_len, hq, d = q.shape
+    n_chunks, hkv, _ = _chunked(k_ring, v_ring, "k_ring", "v_ring", d)
+    _new_rows(q, k_new, v_new, hkv)
+    dev = q.device
+    _pos_tensor(d_pos, dev)
+    out, lse = _outputs(q_len, hq, d, dev, out, lse, want_lse)
+    _on(dev, q=q, k_new=k_new, v_new=v_new, k_ring=k_ring, v_ring=v_ring)
+    ring_size = n_chunks * CHUNK
+    dims = _dims(q, hkv, scale)
+    L = lib()
+    ws, wsb = _ring_workspace(L.verify_attn_ring_workspace_bytes(ctypes.byref(dims), ring_size,
+                                                                 window, num_splits), dev, workspace)
+    check("verify_attn_ring_append_dev", L.verify_attn_ring_append_dev(
+        ctypes.byref(dims), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_ring), _ptr(v_ring),
+        _ptr(d_pos), pos_cap, ring_size, window, num_splits, _ptr(ws), wsb, _ptr(out), _ptr(lse),
+        _stream(stream, dev)))
+    return out, lse
+
+
+def verify_attn_paged_append_dev(q, k_new, v_new, k_pool, v_pool, page_table, d_pos,
+                                 pos_cap: int, *, num_splits: int = 0, scale: float = 0.0,
+                                 out=None, lse=None, want_lse: bool = True, workspace=None,
+                                 stream=None):
+    """verify_kv_append_paged_dev(k_new, v_new, ...) then verify_attn_paged_dev(q, ...) in one
+    launch (plus the split merge): the block's rows are written into their pool slots (from
+    page_table) and attended."""
+    _form(q, "q", torch.bfloat16, (None, None, None))
+    q_len, hq, d = q.shape
+    n_slots, hkv, _ = _chunked(k_pool, v_pool, "k_pool", "v_pool", d)
+    _new_rows(q, k_new, v_new, hkv)
+    _form(page_table, "page_table", torch.int32, (None,))
+    dev = q.device
+    _pos_tensor(d_pos, dev)
+    out, lse = _outputs(q_len, hq, d, dev, out, lse, want_lse)
+    _on(dev, q=q, k_new=k_new, v_new=v_new, k_pool=k_pool, v_pool=v_pool, page_table=page_table)
+    dims = _dims(q, hkv, scale)
+    L = lib()
+    ws, wsb = _workspace(L.verify_attn_paged_workspace_bytes(ctypes.byref(dims), pos_cap + q_len,
+                                                             CHUNK, num_splits), dev, workspace)
+    check("verify_attn_paged_append_dev", L.verify_attn_paged_append_dev(
+        ctypes.byref(dims), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
+        _ptr(page_table), page_table.numel(), n_slots, CHUNK, _ptr(d_pos), pos_cap, num_splits,
+        _ptr(ws), wsb, _ptr(out), _ptr(lse), _stream(stream, dev)))
+    return out, lse
+
+
 def verify_kv_append_ring_dev(k_new, v_new, d_pos, pos_cap: int, k_ring, v_ring, *, stream=None):
     """Append rows k_new, v_new [n][Hkv][D] at positions *d_pos .. (device-resident) to the ring."""
     n, hkv, d = _rows_pair(k_new, v_new, "k_new", "v_new")

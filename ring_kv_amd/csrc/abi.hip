@@ -527,11 +527,29 @@ int32_t verify_attn_paged_partial(const rkv_attn_dims* dims, const void* q,
 
 // ---- one captured step replayed across decode steps: the block position on the device ----
 
-int32_t verify_attn_ring_dev(const rkv_attn_dims* dims, const void* q, const void* k_ring,
-                             const void* v_ring, const int64_t* d_pos, int64_t pos_cap,
-                             int32_t ring_size, int32_t window, int32_t num_splits,
-                             void* workspace, size_t workspace_bytes, float* out, float* lse,
-                             void* stream) {
+// The block's own rows for the calls that append them in the attention launch: both given, and
+// every pointer 16-byte aligned (the rows move as 16-byte pieces).
+static int32_t new_rows_check(const void* k_new, const void* v_new, const void* k, const void* v) {
+  if (k_new == nullptr || v_new == nullptr || k == nullptr || v == nullptr) return RKV_ERR_NULL;
+  if (!aligned16(k_new, v_new, k, v)) return RKV_ERR_ARG;
+  return RKV_OK;
+}
+
+static void set_new_rows(ChunkAttnArgs& a, const void* k_new, const void* v_new, const void* k,
+                         const void* v) {
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.k_w = k_new != nullptr ? static_cast<uint16_t*>(const_cast<void*>(k)) : nullptr;
+  a.v_w = k_new != nullptr ? static_cast<uint16_t*>(const_cast<void*>(v)) : nullptr;
+}
+
+// The ring and pool calls at a device-resident position; k_new, v_new (both or neither): the
+// block's own rows, appended by the same launch.
+static int32_t ring_dev(const rkv_attn_dims* dims, const void* q, const void* k_new,
+                        const void* v_new, const void* k_ring, const void* v_ring,
+                        const int64_t* d_pos, int64_t pos_cap, int32_t ring_size, int32_t window,
+                        int32_t num_splits, void* workspace, size_t workspace_bytes, float* out,
+                        float* lse, void* stream) {
   int32_t st = check_ring(dims, q, k_ring, v_ring, 0, 0, ring_size, window);
   if (st != RKV_OK) return st;
   if (d_pos == nullptr || out == nullptr) return RKV_ERR_NULL;
@@ -564,14 +582,16 @@ int32_t verify_attn_ring_dev(const rkv_attn_dims* dims, const void* q, const voi
   a.d_pos = d_pos;
   a.pos_cap = pos_cap;
   a.ring_size = ring_size;
+  set_new_rows(a, k_new, v_new, k_ring, v_ring);
   return run_chunk_attn(a, dims, part_ws, tickets, out, lse, static_cast<hipStream_t>(stream));
 }
 
-int32_t verify_attn_paged_dev(const rkv_attn_dims* dims, const void* q, const void* k_pool,
-                              const void* v_pool, const int32_t* page_table, int32_t n_table,
-                              int32_t n_slots, int32_t chunk_size, const int64_t* d_pos,
-                              int64_t pos_cap, int32_t num_splits, void* workspace,
-                              size_t workspace_bytes, float* out, float* lse, void* stream) {
+static int32_t paged_dev(const rkv_attn_dims* dims, const void* q, const void* k_new,
+                         const void* v_new, const void* k_pool, const void* v_pool,
+                         const int32_t* page_table, int32_t n_table, int32_t n_slots,
+                         int32_t chunk_size, const int64_t* d_pos, int64_t pos_cap,
+                         int32_t num_splits, void* workspace, size_t workspace_bytes, float* out,
+                         float* lse, void* stream) {
   if (dims == nullptr) return RKV_ERR_NULL;
   if (pos_cap < 0 || pos_cap > INT64_MAX / 2) return RKV_ERR_ARG;
   const int64_t ctx_max = pos_cap + dims->q_len;
@@ -590,7 +610,51 @@ int32_t verify_attn_paged_dev(const rkv_attn_dims* dims, const void* q, const vo
     return RKV_ERR_WORKSPACE;
   a.d_pos = d_pos;
   a.pos_cap = pos_cap;
+  set_new_rows(a, k_new, v_new, k_pool, v_pool);
   return run_chunk_attn(a, dims, workspace, nullptr, out, lse, static_cast<hipStream_t>(stream));
+}
+
+int32_t verify_attn_ring_dev(const rkv_attn_dims* dims, const void* q, const void* k_ring,
+                             const void* v_ring, const int64_t* d_pos, int64_t pos_cap,
+                             int32_t ring_size, int32_t window, int32_t num_splits,
+                             void* workspace, size_t workspace_bytes, float* out, float* lse,
+                             void* stream) {
+  return ring_dev(dims, q, nullptr, nullptr, k_ring, v_ring, d_pos, pos_cap, ring_size, window,
+                  num_splits, workspace, workspace_bytes, out, lse, stream);
+}
+
+int32_t verify_attn_paged_dev(const rkv_attn_dims* dims, const void* q, const void* k_pool,
+                              const void* v_pool, const int32_t* page_table, int32_t n_table,
+                              int32_t n_slots, int32_t chunk_size, const int64_t* d_pos,
+                              int64_t pos_cap, int32_t num_splits, void* workspace,
+                              size_t workspace_bytes, float* out, float* lse, void* stream) {
+  return paged_dev(dims, q, nullptr, nullptr, k_pool, v_pool, page_table, n_table, n_slots,
+                   chunk_size, d_pos, pos_cap, num_splits, workspace, workspace_bytes, out, lse,
+                   stream);
+}
+
+int32_t verify_attn_ring_append_dev(const rkv_attn_dims* dims, const void* q, const void* k_new,
+                                    const void* v_new, void* k_ring, void* v_ring,
+                                    const int64_t* d_pos, int64_t pos_cap, int32_t ring_size,
+                                    int32_t window, int32_t num_splits, void* workspace,
+                                    size_t workspace_bytes, float* out, float* lse, void* stream) {
+  int32_t st = new_rows_check(k_new, v_new, k_ring, v_ring);
+  if (st != RKV_OK) return st;
+  return ring_dev(dims, q, k_new, v_new, k_ring, v_ring, d_pos, pos_cap, ring_size, window,
+                  num_splits, workspace, workspace_bytes, out, lse, stream);
+}
+
+int32_t verify_attn_paged_append_dev(const rkv_attn_dims* dims, const void* q, const void* k_new,
+                                     const void* v_new, void* k_pool, void* v_pool,
+                                     const int32_t* page_table, int32_t n_table, int32_t n_slots,
+                                     int32_t chunk_size, const int64_t* d_pos, int64_t pos_cap,
+                                     int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                     float* out, float* lse, void* stream) {
+  int32_t st = new_rows_check(k_new, v_new, k_pool, v_pool);
+  if (st != RKV_OK) return st;
+  return paged_dev(dims, q, k_new, v_new, k_pool, v_pool, page_table, n_table, n_slots,
+                   chunk_size, d_pos, pos_cap, num_splits, workspace, workspace_bytes, out, lse,
+                   stream);
 }
 
 int32_t attn_merge_partials(const rkv_attn_dims* dims, int32_t num_splits,

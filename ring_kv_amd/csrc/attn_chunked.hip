@@ -203,7 +203,9 @@ __device__ __forceinline__ void merge_share(const ChunkAttnArgs& a, int g, int r
 //   PAGED  slots come from the page table; otherwise the store is a ring (slot = c mod n_slots)
 //   FUSE   the one-launch layer: the workgroups of each (KV head, row tile) merge the tile's
 //          partials once all are stored (see merge_share above); the grid is one-dimensional
-template <int D, int NRG, int KS, bool PAGED, bool FUSE>
+//   APPEND the block's own rows come from k_new / v_new and are written into the store by this
+//          launch (a separate instantiation, so that the other launches carry none of its code)
+template <int D, int NRG, int KS, bool PAGED, bool FUSE, bool APPEND>
 __global__ __launch_bounds__(NRG * KS * 64)
 void chunk_attn_kernel(ChunkAttnArgs a) {
   using T = Tile<D>;
@@ -283,6 +285,44 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
   const int64_t c_lo = c_first + (int64_t)s * a.cps;
   const int64_t c_end = c_first + n_chunks;
   const int nloc = (int)imax64(0, imin64((int64_t)a.cps, c_end - c_lo));
+
+  // ---- the block's own rows, appended by this launch ------------------------------------------
+  // A workgroup whose range of several chunks holds positions of the block writes those rows
+  // into their slots before it reads any chunk (K rows as 16-byte pieces, V into its
+  // dimension-major rows), and waits for the stores: its chunk loads then see them.  Several
+  // workgroups (the row tiles of a range) write the same bytes.  (A one-chunk range lays the
+  // rows over its tile in LDS instead, below.)  A device position out of range writes nothing;
+  // a pool chunk whose table entry lies outside the pool is skipped (the attention masks that
+  // chunk).
+  if (APPEND && !pos_bad && nloc > 1) {
+    const int64_t b_lo = imax64(p0, c_lo * kChunk);
+    const int64_t b_hi = imin64(p0 + a.q_len, (c_lo + nloc) * kChunk);
+    if (b_lo < b_hi) {
+      constexpr int PC = D / 8;                      // 16-byte pieces per row
+      const int nrow = (int)(b_hi - b_lo);
+      for (int u = threadIdx.x; u < nrow * PC; u += NRG * KS * 64) {
+        const int j = u / PC, pc = u % PC;
+        const int64_t pos = b_lo + j;
+        const int64_t c = pos / kChunk;
+        const int64_t slot = PAGED ? (int64_t)a.pt[c] : c % a.n_slots;
+        if (slot < 0 || slot >= a.n_slots) continue;
+        const int off = (int)(pos % kChunk);
+        const int64_t src = ((pos - p0) * a.n_kv_heads + g) * D + pc * 8;
+        const int64_t blk = slot * a.n_kv_heads + g;
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(a.k_new + src);
+        const u32x4 vv = *reinterpret_cast<const u32x4*>(a.v_new + src);
+        *reinterpret_cast<u32x4*>(a.k_w + (blk * kChunk + off) * D + pc * 8) = kv;
+        uint16_t* vd = a.v_w + (blk * D + pc * 8) * kChunk + off;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vd[(2 * e) * kChunk] = (uint16_t)(vv[e] & 0xffffu);
+          vd[(2 * e + 1) * kChunk] = (uint16_t)(vv[e] >> 16);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  }
 
   // ---- this lane's query row (row tile y holds rows 16*NRG*y ..) ---------------------------
   const int row0 = tile * (NRG * 16);
@@ -545,8 +585,63 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
                            : ring_base;
     issue(I0{}, 0, cand);
     load_q();
+    // Block rows in this chunk (appended by this launch): requested with the chunk and Q, laid
+    // over the chunk's tile once it is in LDS, and written into the slot by the first row tile.
+    const int64_t pb_lo = imax64(p0, c_lo * kChunk);
+    const int pnrow = (int)imax64(0, imin64(p0 + a.q_len, (c_lo + 1) * kChunk) - pb_lo);
+    const bool patch = APPEND && !pos_bad && nloc == 1 && pnrow > 0;
+    constexpr int PCS = D / 8;                // 16-byte pieces per row
+    constexpr int MAXU = 2;                   // pieces per thread kept in registers
+    u32x4 pk[MAXU], pv[MAXU];
+    auto new_piece = [&](int e) __attribute__((always_inline)) {
+      return ((pb_lo - p0 + e / PCS) * a.n_kv_heads + g) * D + (e % PCS) * 8;
+    };
+    if (patch) {
+#pragma unroll
+      for (int u = 0; u < MAXU; ++u) {
+        const int e = tid + u * NT;
+        if (e < pnrow * PCS) {
+          pk[u] = *reinterpret_cast<const u32x4*>(a.k_new + new_piece(e));
+          pv[u] = *reinterpret_cast<const u32x4*>(a.v_new + new_piece(e));
+        }
+      }
+    }
     commit(I0{});
     lds_barrier();
+    if (patch) {
+      const bool write = tile == 0 && (unsigned)cand < (unsigned)a.n_slots;
+      const int64_t blk = (int64_t)cand * a.n_kv_heads + g;
+      const int key0 = (int)(pb_lo - c_lo * kChunk);
+      auto lay = [&](int e, const u32x4& kv, const u32x4& vv) __attribute__((always_inline)) {
+        const int key = key0 + e / PCS, pc = e % PCS;
+        uint16_t* buf = &lds[0][0];
+        *reinterpret_cast<u32x4*>(buf + T::k_off(key, pc)) = kv;
+#pragma unroll
+        for (int h2 = 0; h2 < 8; ++h2) {
+          const uint32_t w2 = vv[h2 >> 1];
+          buf[T::v_off(pc * 8 + h2, key >> 3) + (key & 7)] =
+              (uint16_t)((h2 & 1) ? (w2 >> 16) : (w2 & 0xffffu));
+        }
+        if (write) {
+          *reinterpret_cast<u32x4*>(a.k_w + (blk * kChunk + key) * D + pc * 8) = kv;
+          uint16_t* vd = a.v_w + (blk * D + pc * 8) * kChunk + key;
+#pragma unroll
+          for (int h2 = 0; h2 < 8; ++h2) {
+            const uint32_t w2 = vv[h2 >> 1];
+            vd[h2 * kChunk] = (uint16_t)((h2 & 1) ? (w2 >> 16) : (w2 & 0xffffu));
+          }
+        }
+      };
+#pragma unroll
+      for (int u = 0; u < MAXU; ++u) {
+        const int e = tid + u * NT;
+        if (e < pnrow * PCS) lay(e, pk[u], pv[u]);
+      }
+      for (int e = tid + MAXU * NT; e < pnrow * PCS; e += NT)   // blocks of more rows
+        lay(e, *reinterpret_cast<const u32x4*>(a.k_new + new_piece(e)),
+            *reinterpret_cast<const u32x4*>(a.v_new + new_piece(e)));
+      lds_barrier();
+    }
     if (nloc == 1) {
       if (span_edge || (unsigned)cand >= (unsigned)a.n_slots)
         compute(&lds[0][0], 0, cand, std::true_type{});
@@ -794,8 +889,10 @@ hipError_t launch_t(const ChunkAttnArgs& a, hipStream_t stream, bool* merged) {
   const int tiles = (rows + NRG * 16 - 1) / (NRG * 16);
   const dim3 blocks(a.n_kv_heads * a.num_splits, tiles);
   const dim3 threads(NRG * KS * 64);
+  const bool app = a.k_new != nullptr;
   if (a.pt != nullptr)
-    return launch_kernel(chunk_attn_kernel<D, NRG, KS, true, false>, blocks, threads, a, stream);
+    return app ? launch_kernel(chunk_attn_kernel<D, NRG, KS, true, false, true>, blocks, threads, a, stream)
+               : launch_kernel(chunk_attn_kernel<D, NRG, KS, true, false, false>, blocks, threads, a, stream);
   // the one-launch ring layer: counters given, few enough splits for the merge's registers,
   // (KV head, row tile) groups that divide evenly over the XCDs, and a grid that fits one
   // workgroup per compute unit (every workgroup of a group is resident while the others wait)
@@ -804,10 +901,12 @@ hipError_t launch_t(const ChunkAttnArgs& a, hipStream_t stream, bool* merged) {
       a.num_splits <= kFuseMaxSplits && groups % kXcds == 0 &&
       groups * kTicketStride <= (int64_t)kTicketBytes && groups * a.num_splits <= a.fill_wgs) {
     *merged = true;
-    return launch_kernel(chunk_attn_kernel<D, NRG, KS, false, true>,
-                         dim3((unsigned)(groups * a.num_splits)), threads, a, stream);
+    const dim3 grid((unsigned)(groups * a.num_splits));
+    return app ? launch_kernel(chunk_attn_kernel<D, NRG, KS, false, true, true>, grid, threads, a, stream)
+               : launch_kernel(chunk_attn_kernel<D, NRG, KS, false, true, false>, grid, threads, a, stream);
   }
-  return launch_kernel(chunk_attn_kernel<D, NRG, KS, false, false>, blocks, threads, a, stream);
+  return app ? launch_kernel(chunk_attn_kernel<D, NRG, KS, false, false, true>, blocks, threads, a, stream)
+             : launch_kernel(chunk_attn_kernel<D, NRG, KS, false, false, false>, blocks, threads, a, stream);
 }
 
 // Tiles of 64 rows (blockIdx.y), two waves per row group (key halves).  Tiles of one split

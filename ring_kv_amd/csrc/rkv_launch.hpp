@@ -59,6 +59,13 @@ struct ChunkAttnArgs {
   // launch): one int per (KV head, row tile), each in a 128-byte line of its own, zero before
   // the launch and left zero by it.
   int32_t* tickets;
+  // The block's own K/V rows (nullptr: the store already holds them), [q_len][Hkv][D] bf16 for
+  // positions p0 .. p0 + q_len - 1: written into their slots of the store (k_w, v_w: the same
+  // memory as k, v) before they are read, so that the append and the attention are one launch.
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint16_t* k_w;
+  uint16_t* v_w;
 };
 
 // Blocks of up to kVerifyMaxRows rows per KV head (a verify block: q_len * G) run the

@@ -281,3 +281,15 @@ def test_device_position_checks():
     assert ap(cap=113) == ETABLE                          # 113 + 16 - 1 = 128: chunk 2
     assert L.verify_pos_advance(NULL, P, NULL) == ENULL
     assert L.verify_pos_advance(P, NULL, NULL) == ENULL
+    # the append inside the attention launch: both row pointers, 16-byte alignment, then the
+    # checks of the attention call itself
+    odd = ctypes.c_void_p(0x1008)
+    rr = lambda kn=P, vn=P, store=P, pos=P, ws=P: L.verify_attn_ring_append_dev(  # noqa: E731
+        dims(), P, kn, vn, store, P, pos, 200000, 2048, 512, 0, ws, ws_ring, P, NULL, NULL)
+    assert rr(kn=NULL) == ENULL and rr(vn=NULL) == ENULL and rr(store=NULL) == ENULL
+    assert rr(kn=odd) == EARG and rr(store=odd) == EARG
+    assert rr(pos=NULL) == ENULL and rr(ws=NULL) == EWS
+    pr = lambda kn=P, vn=P, pos=P, cap=cap: L.verify_attn_paged_append_dev(  # noqa: E731
+        dims(), P, kn, vn, P, P, P, 2048, 2048, 64, pos, cap, 0, P, ws_pool, P, NULL, NULL)
+    assert pr(kn=NULL) == ENULL and pr(vn=odd) == EARG
+    assert pr(pos=NULL) == ENULL and pr(cap=cap + 1) == ETABLE

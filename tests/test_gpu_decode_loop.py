@@ -42,7 +42,8 @@ def _close(got, want, what):
     return err, lerr
 
 
-def test_one_graph_replayed_over_decode_steps():
+@pytest.mark.parametrize("fused", [False, True], ids=["append_then_attend", "append_in_attention"])
+def test_one_graph_replayed_over_decode_steps(fused):
     """Four layers (three window layers over 2,048-slot rings, one full-attention layer over a
     permuted pool) at a context of 9,000 committed positions; ten decode steps from one graph.
     Each step: the block's 16 K/V rows are appended at the device position in every layer, each
@@ -50,7 +51,9 @@ def test_one_graph_replayed_over_decode_steps():
     the position advances by a + 1 on the device.  The block is the last committed token and 15
     drafts (rows at positions P .. P+15), so the a accepted drafts keep rows P .. P+a, all of them
     written by this step's append, and the next block starts at P + a + 1.  The host copies step
-    k's inputs into the captured buffers and replays; nothing else changes between steps."""
+    k's inputs into the captured buffers and replays; nothing else changes between steps.  Run
+    with the append and the attention as two calls per layer, and as one (the append inside the
+    attention launch)."""
     g = np.random.default_rng(2026)
     kinds = ["ring", "ring", "ring", "paged"]
     P0, N, V = 9000, 10, 4096
@@ -104,7 +107,13 @@ def test_one_graph_replayed_over_decode_steps():
     def step():
         for i, kind in enumerate(kinds):
             k_st, v_st = gpu[i]
-            if kind == "ring":
+            if fused and kind == "ring":
+                rk.verify_attn_ring_append_dev(qb[i], kb[i], vb[i], k_st, v_st, d_pos, pos_cap, W,
+                                               out=outs[i], lse=lses[i], workspace=ws_r)
+            elif fused:
+                rk.verify_attn_paged_append_dev(qb[i], kb[i], vb[i], k_st, v_st, d_pt, d_pos,
+                                                pos_cap, out=outs[i], lse=lses[i], workspace=ws_p)
+            elif kind == "ring":
                 rk.verify_kv_append_ring_dev(kb[i], vb[i], d_pos, pos_cap, k_st, v_st)
                 rk.verify_attn_ring_dev(qb[i], k_st, v_st, d_pos, pos_cap, W, out=outs[i],
                                         lse=lses[i], workspace=ws_r)
@@ -250,3 +259,83 @@ def test_launch_status_ignores_an_earlier_error():
     torch.cuda.synchronize()
     want = oracle.attention_ring(c.q, c.k_ring, c.v_ring, 30000, 30000 % R, R, W)
     _close((out.cpu().numpy(), lse.cpu().numpy()), want, "ring after an earlier error")
+
+
+@pytest.mark.parametrize("P", [130040, 130048, 9000, 40])
+def test_ring_append_in_attention_equals_two_calls(P):
+    """The block's rows appended by the attention launch: the same outputs and the same ring as
+    verify_kv_append_ring_dev followed by verify_attn_ring_dev (blocks inside one chunk and
+    across a chunk boundary, near the ring's start), and the oracle's append + attention."""
+    g = np.random.default_rng(P)
+    kn, vn = _bits(g, (Q, HKV, D)), _bits(g, (Q, HKV, D))
+    c = ring_case(63, 0, P, Q, HQ, HKV, D, R, W, keep_rows=False)
+    q, dkn, dvn = dev(c.q), dev(kn), dev(vn)
+    k1, v1 = dev(c.k_ring), dev(c.v_ring)
+    k2, v2 = k1.clone(), v1.clone()
+    cap = P + 3 * Q
+    d_pos = torch.tensor([P], dtype=torch.int64, device="cuda")
+    dims = AttnDims(Q, HQ, HKV, D, 0.0, 1)
+    full = rk.lib().verify_attn_ring_workspace_bytes(ctypes.byref(dims), R, W, 0)
+    ws1 = torch.zeros(full, dtype=torch.uint8, device="cuda")
+    ws2 = torch.zeros(full, dtype=torch.uint8, device="cuda")
+    say(f"ring append in attention P={P}")
+    rk.verify_kv_append_ring_dev(dkn, dvn, d_pos, cap, k1, v1)
+    o1, l1 = rk.verify_attn_ring_dev(q, k1, v1, d_pos, cap, W, workspace=ws1)
+    o2, l2 = rk.verify_attn_ring_append_dev(q, dkn, dvn, k2, v2, d_pos, cap, W, workspace=ws2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), "outputs differ from the two calls"
+    # bit patterns: slots that hold no position are NaN
+    assert torch.equal(k1.view(torch.int16), k2.view(torch.int16)), "ring K differs"
+    assert torch.equal(v1.view(torch.int16), v2.view(torch.int16)), "ring V differs"
+    kr, vr = oracle.append_ring(c.k_ring, c.v_ring, kn, vn, P)
+    np.testing.assert_array_equal(_host(k2), kr)
+    np.testing.assert_array_equal(_host(v2), vr)
+    _close((o2.cpu().numpy(), l2.cpu().numpy()),
+           oracle.attention_ring(c.q, kr, vr, P, P % R, R, W), f"ring append in attention P={P}")
+
+
+@pytest.mark.parametrize("P", [8184, 8192, 100, 40])
+def test_paged_append_in_attention_equals_two_calls(P):
+    """As above over a permuted pool whose table already holds the block's chunks."""
+    g = np.random.default_rng(P + 1)
+    kn, vn = _bits(g, (Q, HKV, D)), _bits(g, (Q, HKV, D))
+    cap = P + 3 * Q
+    ctx = P + Q
+    n = -(-(cap + Q) // CH)                    # chunks any position up to the cap can reach
+    c = paged_case(64, 0, ctx, Q, HQ, HKV, D, n_slots=n + 7, keep_rows=False)
+    pt = np.concatenate([c.page_table, np.setdiff1d(np.arange(n + 7), c.page_table)])[:n]
+    pt = pt.astype(np.int32)
+    q, dkn, dvn, d_pt = dev(c.q), dev(kn), dev(vn), dev(pt)
+    k1, v1 = dev(c.k_pool), dev(c.v_pool)
+    k2, v2 = k1.clone(), v1.clone()
+    d_pos = torch.tensor([P], dtype=torch.int64, device="cuda")
+    say(f"paged append in attention P={P}")
+    rk.verify_kv_append_paged_dev(dkn, dvn, d_pos, cap, k1, v1, d_pt)
+    o1, l1 = rk.verify_attn_paged_dev(q, k1, v1, d_pt, d_pos, cap)
+    o2, l2 = rk.verify_attn_paged_append_dev(q, dkn, dvn, k2, v2, d_pt, d_pos, cap)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), "outputs differ from the two calls"
+    assert torch.equal(k1.view(torch.int16), k2.view(torch.int16)), "pool K differs"
+    assert torch.equal(v1.view(torch.int16), v2.view(torch.int16)), "pool V differs"
+    kp, vp = oracle.append_paged(c.k_pool, c.v_pool, pt, kn, vn, P)
+    np.testing.assert_array_equal(_host(k2), kp)
+    np.testing.assert_array_equal(_host(v2), vp)
+    _close((o2.cpu().numpy(), l2.cpu().numpy()), oracle.attention_paged(c.q, kp, vp, pt, ctx),
+           f"paged append in attention P={P}")
+
+
+def test_append_in_attention_outside_the_cap_writes_nothing():
+    """A device position above the cap: no row is written and the attention is NaN."""
+    g = np.random.default_rng(77)
+    kn, vn = _bits(g, (Q, HKV, D)), _bits(g, (Q, HKV, D))
+    c = ring_case(65, 0, 30000, Q, HQ, HKV, D, R, W, keep_rows=False)
+    q, dkn, dvn = dev(c.q), dev(kn), dev(vn)
+    kr, vr = dev(c.k_ring), dev(c.v_ring)
+    k0, v0 = kr.clone(), vr.clone()
+    d_pos = torch.tensor([30100], dtype=torch.int64, device="cuda")
+    say("ring append in attention outside the cap")
+    o, l = rk.verify_attn_ring_append_dev(q, dkn, dvn, kr, vr, d_pos, 30000, W)
+    torch.cuda.synchronize()
+    assert torch.equal(kr.view(torch.int16), k0.view(torch.int16))
+    assert torch.equal(vr.view(torch.int16), v0.view(torch.int16))
+    assert torch.isnan(o).all() and torch.isnan(l).all()
