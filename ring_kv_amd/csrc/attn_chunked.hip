@@ -102,9 +102,9 @@ struct Tile {
 constexpr int kHwRegXccId = 20 | (31 << 11);
 
 // Counter word of a (KV head, row tile) group in the one-launch ring layer: arrivals (bits
-// 0..4), departures (bits 5..9), the sum of the arrivals' XCD ids (bits 10..17) and of their
-// squares (bits 18..29).  Equal sums of ids and of squared ids (S times one id and S times its
-// square) force every id to be that one.
+// 0..4), departures (bits 5..9), the sum of the arrivals' XCD ids plus one (bits 10..17, at most
+// 12 x 16) and of their squares (bits 18..29, at most 12 x 256).  Equal sums of ids and of
+// squared ids (S times one id and S times its square) force every id to be that one.
 constexpr int kArrive = 1;
 constexpr int kDepart = 1 << 5;
 constexpr int kSpinLimit = 1 << 17;    // polls before a workgroup gives up (NaN rows)
@@ -860,7 +860,9 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
     int* const ticket = a.tickets + grp * (kTicketStride / 4);
     const int S = a.num_splits;
     if (tid == 0) {
-      const int x = (int)((uint32_t)__builtin_amdgcn_s_getreg(kHwRegXccId) & 15u);
+      // the XCD id plus one, so that no id sums to zero (a counter that was not zeroed cannot
+      // pass for a complete group)
+      const int x = (int)((uint32_t)__builtin_amdgcn_s_getreg(kHwRegXccId) & 15u) + 1;
       const int arrive = kArrive + (x << 10) + ((x * x) << 18);
       int v = __hip_atomic_fetch_add(ticket, arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) +
               arrive;

@@ -106,3 +106,23 @@ def test_one_launch_graph_replays():
         assert int(ws[:COUNTER_BYTES].count_nonzero()) == 0, f"replay {k}: counters"
     assert_attn_close((out.cpu().numpy(), lse.cpu().numpy()), run_oracle(c), "bf16",
                       "ring one launch replayed")
+
+
+def test_counters_not_zeroed_give_nan_not_mixed_rows():
+    """Counters the caller did not zero (every byte 0x18 here: more arrivals than the group has)
+    cannot pass for a complete group: the layer writes NaN rather than rows merged from partials
+    that may not be there.  Zeroed again, the same workspace gives the exact result."""
+    c = ring_case(973, 0, 30000, 16, 16, 4, 128, 2048, 512)
+    q, kr, vr = dev(c.q), dev(c.k_ring), dev(c.v_ring)
+    full = _ws_bytes(c)
+    ws = torch.full((full,), 0x18, dtype=torch.uint8, device="cuda")
+    say("ring one launch: counters not zeroed")
+    o, l = rk.verify_attn_ring(q, kr, vr, 30000, 512, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(o).all() and torch.isnan(l).all()
+    ws[:COUNTER_BYTES].zero_()
+    o2, l2 = rk.verify_attn_ring(q, kr, vr, 30000, 512, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws[:COUNTER_BYTES].count_nonzero()) == 0
+    assert_attn_close((o2.cpu().numpy(), l2.cpu().numpy()), run_oracle(c), "bf16",
+                      "ring one launch after zeroing")
