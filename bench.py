@@ -441,7 +441,7 @@ def config_timings(torch, rk, synth, probe, n_small, n_large):
     entry("ring_w512_r2048", [lambda: rk.verify_attn_ring(q2, kr, vr, c.pos0, c.window, out=o,
                                                           lse=l, workspace=wsr)],
           n_small, c.kv_bytes, attn_flops(c), 2500.0, "mfma_bf16",
-          "verify_attn_ring, one chunk per split + merge; bound: launch latency")
+          "verify_attn_ring, one chunk per split, merged in the same launch; bound: launch latency")
     # C3: paged 8K
     c3, _ = synth.workload("paged_8k", keep_rows=False)
     q3, kp3, vp3, pt3 = t(c3.q), t(c3.k_pool), t(c3.v_pool), t(c3.page_table)
