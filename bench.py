@@ -13,15 +13,15 @@ live with HIP events on the stream it runs on), the step by layer type, 1,024-to
 blocks through the pool and the ring (with their own matrix-core roofline), host paging of
 chunks over PCIe and the verify over 8K resident of 256K, the four single-layer
 workloads timed one by one (cold and warm, median / p10 / p90), a measured HBM read bandwidth,
-and the fp64 oracle timed on the host cores over a bounded sample of the same workload (plus one
-call per single-layer workload).
+and the fp64 oracle timed on the host cores over a bounded sample of the same workload (plus its
+wall time per single-layer workload).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload stack_40l_131k|paged_256k]
     python bench.py --mode copy     # plain 1-GiB device copies, for HBM counter calibration
     python bench.py --mode kernel   # the dominant kernel alone (10 launches), for counter runs
     python bench.py --mode prefill-kernel   # the prefill kernel alone at 131,072 (3 launches)
     python bench.py --mode configs  # each single-layer workload and block append (16 and 1,024
-                                    # rows) called 100 times (30 at 256K, for the prefill blocks
+                                    # rows) called 200 times (51 at 256K, for the prefill blocks
                                     # and for a page-out and page-in of 128 chunks), a
                                     # cache-evicting read before each, for a kernel trace
     python bench.py --mode traffic --fetch F.csv --write W.csv --copy-fetch CF.csv --copy-write CW.csv
@@ -44,6 +44,11 @@ METRIC = "KV GB/s (% of HBM peak) for 16-token verify attention; µs/layer at 25
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_chunk_attn_paged_131k.json")
 KERNEL_SRC = os.path.join(ROOT, "ring_kv_amd", "csrc", "attn_chunked.hip")
+# timed calls per single-layer workload: 200 for the short ones, 51 (a multiple of the three
+# pool copies) for the 262,144-context layer, the prefill blocks and the paging calls
+N_SMALL, N_LARGE = 200, 51
+# replays behind the step's per-step distribution (at least this many, or --steps if more)
+N_STEP_DIST = 50
 
 
 def log(*a):
@@ -369,7 +374,7 @@ def config_timings(torch, rk, synth, probe, n_small, n_large):
     them, minus a graph of the reads alone; the 256K pool also rotates over three copies.  Mean
     µs per call, launch gaps included.  Beside them, the device's own kernel time per call (the
     call's kernel durations summed, from the in-process kernel records), warm and cold: median,
-    p10, p90 over 30 calls."""
+    p10, p90 over the same n calls (200 for the small workloads, 51 at 256K)."""
     t = lambda a: rk.tensor_from_numpy(a, "cuda")  # noqa: E731
     scratch = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
     flush = lambda: probe.read(scratch)  # noqa: E731
@@ -393,9 +398,8 @@ def config_timings(torch, rk, synth, probe, n_small, n_large):
         e = {"us_warm": round(warm, 2), "calls_per_graph": n, "note": note}
         # the device's own kernel time per call (the sum of the call's kernel durations, as a
         # kernel trace gives them): back to back (warm) and after a cache-evicting read (cold)
-        m = min(n, 30)
-        kw, _ = kernel_times(torch, op, m)
-        kc, _ = kernel_times(torch, op, m, pre=flush)
+        kw, _ = kernel_times(torch, op, n)
+        kc, _ = kernel_times(torch, op, n, pre=flush)
         if kw and kc:
             e["kernel_us_warm"] = dist(kw)
             e["kernel_us_cold"] = dist(kc)
@@ -734,24 +738,31 @@ def cpu_info():
 
 
 def oracle_per_config(synth, oracle):
-    """One timed oracle call per single-layer workload (µs of wall time)."""
+    """The oracle's wall time per single-layer workload (µs): the median of three timed calls
+    for the short workloads, one call at 262,144."""
+    import statistics
+
+    def timed(f, calls):
+        ts = []
+        for _ in range(calls):
+            t0 = time.perf_counter()
+            f()
+            ts.append((time.perf_counter() - t0) * 1e6)
+        return round(statistics.median(ts), 1)
+
     res = {}
     c, acc = synth.workload("contig_1k_f32")
-    t0 = time.perf_counter()
-    oracle.attention_contiguous(c.q, c.k_rows, c.v_rows, c.ctx_len, window=c.window, dtype=c.dtype)
-    res["contig_1k_f32"] = round((time.perf_counter() - t0) * 1e6, 1)
-    t0 = time.perf_counter()
-    oracle.greedy_accept(acc.logits, acc.proposals)
-    res["accept_17x4096"] = round((time.perf_counter() - t0) * 1e6, 1)
-    for name in ("ring_w512_r2048", "paged_8k", "paged_256k"):
+    res["contig_1k_f32"] = timed(lambda: oracle.attention_contiguous(
+        c.q, c.k_rows, c.v_rows, c.ctx_len, window=c.window, dtype=c.dtype), 3)
+    res["accept_17x4096"] = timed(lambda: oracle.greedy_accept(acc.logits, acc.proposals), 3)
+    for name, calls in (("ring_w512_r2048", 3), ("paged_8k", 3), ("paged_256k", 1)):
         c, _ = synth.workload(name, keep_rows=False)
-        t0 = time.perf_counter()
         if c.kind == "ring":
-            oracle.attention_ring(c.q, c.k_ring, c.v_ring, c.pos0, c.ring_head, c.ring_size,
-                                  c.window)
+            res[name] = timed(lambda: oracle.attention_ring(
+                c.q, c.k_ring, c.v_ring, c.pos0, c.ring_head, c.ring_size, c.window), calls)
         else:
-            oracle.attention_paged(c.q, c.k_pool, c.v_pool, c.page_table, c.ctx_len)
-        res[name] = round((time.perf_counter() - t0) * 1e6, 1)
+            res[name] = timed(lambda: oracle.attention_paged(
+                c.q, c.k_pool, c.v_pool, c.page_table, c.ctx_len), calls)
         del c
     return res
 
@@ -939,7 +950,7 @@ def main():
         return
 
     if args.mode == "configs":
-        config_calls(torch, rk, synth, ReadProbe(torch), 100, 30)
+        config_calls(torch, rk, synth, ReadProbe(torch), N_SMALL, N_LARGE)
         print(json.dumps({"mode": "configs"}), flush=True)
         return
 
@@ -971,7 +982,7 @@ def main():
             step_fn = st.step
         # the step's distribution: events around each replay; the device's kernel time per step
         # (the sum of its 82 kernels' durations) from the in-process kernel records
-        per_step = per_call_ms(step_fn, args.steps, torch)
+        per_step = per_call_ms(step_fn, max(N_STEP_DIST, args.steps), torch)
         k_step, k_by = kernel_times(torch, step_fn, min(5, args.steps))
         # dominant kernel: the paged split-K kernel at 131,072 over the 10 paged layers, three
         # rounds of 10 launches in one HIP graph; HIP events on the replay stream (launch gaps
@@ -1127,11 +1138,11 @@ def main():
     if not args.no_configs:
         log("single-layer workloads, cold and warm")
         probe = ReadProbe(torch)
-        res["configs_gpu"] = config_timings(torch, rk, synth, probe, 100, 30)
+        res["configs_gpu"] = config_timings(torch, rk, synth, probe, N_SMALL, N_LARGE)
         res["read_bw_probe"] = read_bw_probe(torch, probe)
         if "us_per_layer_256k" in res:
             # The headline 256K figure: the layer's two kernels (split + merge), their own
-            # durations summed per call, caches evicted before each call (median of 30 calls
+            # durations summed per call, caches evicted before each call (median of 51 calls
             # over three pool copies).  Alongside: the cold graph figure (calls in a graph minus a
             # graph of the evicting reads: launch gaps included) and the back-to-back graph
             # figure (long series of this kernel reach the card's power limit).
