@@ -148,7 +148,9 @@ int32_t decode_attn_ref_layout(const rkv_attn_dims* dims, const void* q, const v
  * Workspace (caller-owned device memory, needed when the span is split): a workspace of at
  * least verify_attn_ring_workspace_bytes() bytes starts with RKV_RING_COUNTER_BYTES of
  * counters, which must be zero before the workspace's first use and which every call leaves
- * zero; with them the call merges the partials inside its one launch where it can (the
+ * ready for the next (each 128-byte group line: an arrival count, returned to zero, and a
+ * generation word that moves by one per call); with them the call merges the partials inside
+ * its one launch where it can (the
  * workgroups of each KV head and row tile, all on one XCD, wait for each other's partials and
  * each merges a share of the tile's rows; used when the grid fits one workgroup per compute
  * unit).  Calls that share a workspace must not overlap, and the counters must not be written

@@ -308,8 +308,8 @@ static int64_t ring_max_chunks(const rkv_attn_dims* d, int32_t window) {
   return (span + kChunk - 2) / kChunk + 1;
 }
 
-// A ring call's workspace: kTicketBytes of counters (zero before the workspace's first use,
-// left zero by every call), then the partials of the widest span's split layout.
+// A ring call's workspace: kTicketBytes of counters (zero before the workspace's first use; every
+// call leaves its arrival counters zero), then the partials of the widest span's split layout.
 static size_t ring_workspace_full(const rkv_attn_dims* dims, int32_t window, int32_t num_splits) {
   int32_t s, cps;
   choose_splits(ring_max_chunks(dims, window), auto_split_target(dims, kRing), num_splits, &s,

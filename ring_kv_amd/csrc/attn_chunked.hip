@@ -101,12 +101,15 @@ struct Tile {
 // hardware register XCC_ID (id 20, all 32 bits): the XCD the wave runs on
 constexpr int kHwRegXccId = 20 | (31 << 11);
 
-// Counter word of a (KV head, row tile) group in the one-launch ring layer: arrivals (bits
-// 0..4), departures (bits 5..9), the sum of the arrivals' XCD ids plus one (bits 10..17, at most
-// 12 x 16) and of their squares (bits 18..29, at most 12 x 256).  Equal sums of ids and of
-// squared ids (S times one id and S times its square) force every id to be that one.
+// The counter line of a (KV head, row tile) group in the one-launch ring layer holds two words.
+// Word 0 counts this launch's arrivals (bits 0..4) and sums the arrivals' XCD ids plus one
+// (bits 10..17, at most 12 x 16) and their squares (bits 18..29, at most 12 x 256): equal sums of
+// ids and of squared ids (S times one id and S times its square) force every id to be that one.
+// The last arrival resets it to zero.  Word kGenWord is a generation that only the last arrival
+// of a launch moves (by 1 if the group checked out, by 2 if not), so the others wait for it to
+// move from the value they read before arriving; it needs no reset.
 constexpr int kArrive = 1;
-constexpr int kDepart = 1 << 5;
+constexpr int kGenWord = 16;           // ints: the generation sits 64 bytes into the line
 constexpr int kSpinLimit = 1 << 17;    // polls before a workgroup gives up (NaN rows)
 
 // cache policy sc1 of a buffer store (gfx950): written through the XCD's L2
@@ -242,6 +245,7 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
   const int lq = lane >> 4;
 
   int g, s, tile, grp = 0;
+  uint32_t gen0 = 0;               // FUSE: the group's generation before this launch's arrivals
   if constexpr (FUSE) {
     // The S workgroups of group grp = (KV head, row tile) are blocks x, x + 8, x + 16, ... of
     // one residue x mod 8: the dispatcher deals blocks round-robin over the 8 XCDs, so a group
@@ -252,6 +256,10 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
     s = j % a.num_splits;
     g = grp % a.n_kv_heads;
     tile = grp / a.n_kv_heads;
+    // read now, long before this workgroup arrives: only the group's last arrival moves it
+    if (tid == 0)
+      gen0 = (uint32_t)__hip_atomic_fetch_add(a.tickets + grp * (kTicketStride / 4) + kGenWord, 0,
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else {
     const int b = xcd_block(blockIdx.x, gridDim.x);
     g = b % a.n_kv_heads;
@@ -873,38 +881,45 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
     if ((KS == 1 || kh == 0) && wave_active && row_ok) store_rows();
     // ---- the group merges its partials once all of them are stored ---------------------------
     // A workgroup's stores reach the XCD's L2 (the L1 writes through) once acknowledged; its
-    // arrival follows every thread's acknowledgement.  Every workgroup of the group then waits
-    // (a bounded poll) for the group's S arrivals and merges its share of the tile's rows.  The
-    // group's workgroups are all resident at once (the launch is used only when its grid fits
-    // one workgroup per compute unit), so the wait ends when the slowest of them arrives.  The
-    // last to leave resets the counter to zero.
+    // arrival follows every thread's acknowledgement.  The last of the group's S arrivals checks
+    // the group and moves the generation; the others wait for it to move (a bounded poll) and
+    // then every workgroup merges its share of the tile's rows.  The group's workgroups are all
+    // resident at once (the launch is used only when its grid fits one workgroup per compute
+    // unit), so the wait ends when the slowest of them arrives.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     int* const ticket = a.tickets + grp * (kTicketStride / 4);
+    int* const gen = ticket + kGenWord;
     const int S = a.num_splits;
     if (tid == 0) {
       // the XCD id plus one, so that no id sums to zero (a counter that was not zeroed cannot
       // pass for a complete group)
       const int x = (int)((uint32_t)__builtin_amdgcn_s_getreg(kHwRegXccId) & 15u) + 1;
-      const int arrive = kArrive + (x << 10) + ((x * x) << 18);
-      int v = __hip_atomic_fetch_add(ticket, arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) +
-              arrive;
-      for (int polls = 0; (v & 31) < S && polls < kSpinLimit; ++polls) {
-        __builtin_amdgcn_s_sleep(2);
-        v = __hip_atomic_fetch_add(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      int arrive = kArrive + (x << 10) + ((x * x) << 18);
+      // the arrival depends on the generation read at the start, so it is issued only once that
+      // read has returned: every workgroup reads the generation before the last arrival moves it
+      asm volatile("" : "+v"(arrive) : "v"(gen0));
+      const int v = __hip_atomic_fetch_add(ticket, arrive, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT) + arrive;
+      int flag;
+      if ((v & 31) == S) {
+        const bool all_here = ((v >> 10) & 255) == S * x && ((v >> 18) & 4095) == S * x * x;
+        __hip_atomic_store(gen, (int)(gen0 + (all_here ? 1u : 2u)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        flag = all_here ? 1 : 2;
+      } else {
+        uint32_t gv = gen0;
+        for (int polls = 0; gv == gen0 && polls < kSpinLimit; ++polls) {
+          __builtin_amdgcn_s_sleep(2);
+          gv = (uint32_t)__hip_atomic_fetch_add(gen, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        flag = gv - gen0 == 1u ? 1 : 2;
       }
-      const bool all_here = (v & 31) == S && ((v >> 10) & 255) == S * x &&
-                            ((v >> 18) & 4095) == S * x * x;
-      merge_flag = all_here ? 1 : 2;
+      merge_flag = flag;
     }
     __syncthreads();
-    const int f = merge_flag;
-    int dep = 0;
-    if (tid == 0)     // leave; the returned count is looked at after the merge
-      dep = __hip_atomic_fetch_add(ticket, kDepart, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    merge_share<D, NRG * KS * 64, NRG * 16>(a, g, row0, s, f == 2);
-    if (tid == 0 && ((dep >> 5) & 31) == S - 1)
-      __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    merge_share<D, NRG * KS * 64, NRG * 16>(a, g, row0, s, merge_flag == 2);
   }
 }
 

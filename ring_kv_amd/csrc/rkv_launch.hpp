@@ -56,8 +56,8 @@ struct ChunkAttnArgs {
   int32_t ring_size;      // positions the ring holds (ring only)
   int32_t fill_wgs;       // workgroups of one round over the device (its compute units)
   // Counters of the one-launch ring layer (nullptr: the partials are merged by a second
-  // launch): one int per (KV head, row tile), each in a 128-byte line of its own, zero before
-  // the launch and left zero by it.
+  // launch): a 128-byte line per (KV head, row tile) holding an arrival counter (zero before
+  // the launch and left zero by it) and a generation word (any value).
   int32_t* tickets;
   // The block's own K/V rows (nullptr: the store already holds them), [q_len][Hkv][D] bf16 for
   // positions p0 .. p0 + q_len - 1: written into their slots of the store (k_w, v_w: the same
