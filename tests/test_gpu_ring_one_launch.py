@@ -133,3 +133,24 @@ def test_counters_not_zeroed_give_nan_not_mixed_rows():
     assert _arrivals_zero(ws)
     assert_attn_close((o2.cpu().numpy(), l2.cpu().numpy()), run_oracle(c), "bf16",
                       "ring one launch after zeroing")
+
+
+def test_one_workspace_across_split_counts():
+    """One workspace serves calls whose split counts differ (positions whose window spans 2 to 10
+    chunks, in an order that goes up and down): each call's arrival counters start from zero
+    whatever the previous call's split count was, and each call gives the two-launch bits."""
+    dims = AttnDims(16, 16, 4, 128, 0.0, 1)
+    full = rk.lib().verify_attn_ring_workspace_bytes(ctypes.byref(dims), 2048, 512, 0)
+    ws = torch.zeros(full, dtype=torch.uint8, device="cuda")
+    for k, pos0 in enumerate((30000, 100, 30720, 470, 2040, 30016, 60, 30000)):
+        c = ring_case(974 + k, pos0, pos0, 16, 16, 4, 128, 2048, 512)
+        q, kr, vr = dev(c.q), dev(c.k_ring), dev(c.v_ring)
+        say(f"ring one launch, shared workspace: pos0={pos0}")
+        o1, l1 = rk.verify_attn_ring(q, kr, vr, pos0, 512, workspace=ws)
+        o2, l2 = rk.verify_attn_ring(q, kr, vr, pos0, 512,
+                                     workspace=torch.empty(full - COUNTER_BYTES,
+                                                           dtype=torch.uint8, device="cuda"))
+        torch.cuda.synchronize()
+        assert _arrivals_zero(ws), f"pos0={pos0}: counters"
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), f"pos0={pos0}: one launch differs"
+        assert not torch.isnan(o1).any()
