@@ -81,9 +81,10 @@ constexpr int kPrefillTileRows = 256;
 constexpr int kFuseMaxSplits = 12;
 constexpr int kXcds = 8;
 // Bytes of counters the one-launch ring layer keeps at the start of a ring call's workspace: one
-// int per (KV head, row tile) every kTicketStride bytes (the counters of different groups never
-// share a cache line: every workgroup's add goes to the device-wide coherence point, and adds to
-// one line queue there), for up to 64 groups.
+// kTicketStride-byte line per (KV head, row tile), holding the group's arrival counter and its
+// generation word (the lines of different groups never share a cache line: every workgroup's
+// add goes to the device-wide coherence point, and adds to one line queue there), for up to 64
+// groups.
 constexpr size_t kTicketBytes = RKV_RING_COUNTER_BYTES;
 constexpr int kTicketStride = 128;
 // Row tile of the prefill kernel: kPrefillTileRows, or half of it (two waves per row group, one
