@@ -839,39 +839,33 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
     const float inv = pos_bad ? __builtin_nanf("") : (l > 0.f ? 1.f / l : 0.f);
     const float lse_nat = pos_bad ? __builtin_nanf("")
                                   : (lfr > 0.f ? (m_run + log2f(lfr)) * kLn2 : -INFINITY);
-    float* dst;
     if (a.part_o == nullptr) {
-      dst = a.out + ((int64_t)qi * a.n_q_heads + hq) * D;
+      float* dst = a.out + ((int64_t)qi * a.n_q_heads + hq) * D;
       if (a.lse != nullptr && lq == 0) a.lse[(int64_t)qi * a.n_q_heads + hq] = lse_nat;
-    } else {
-      const int64_t prow = ((int64_t)g * a.num_splits + s) * rows + r;
-      if constexpr (!FUSE) {
-        // Partials for a merge launch: written through the XCD's L2 (cache policy sc1), which
-        // the kernel's end then need not write back (measured: a launch storing 8 MiB ends
-        // ~0.6 us sooner).  Buffer bases are this (KV head, split)'s block of rows.
-        const int64_t blk = ((int64_t)g * a.num_splits + s) * rows;
-        const __amdgpu_buffer_rsrc_t po =
-            __builtin_amdgcn_make_buffer_rsrc(a.part_o + blk * D, 0, rows * D * 4, 0x00020000);
-        const __amdgpu_buffer_rsrc_t pl =
-            __builtin_amdgcn_make_buffer_rsrc(a.part_lse + blk, 0, rows * 4, 0x00020000);
-        if (lq == 0)
-          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse_nat), pl, r * 4,
-                                                0, kSc1);
 #pragma unroll
-        for (int t = 0; t < TMD; ++t) {
-          f32x4 o = oacc[t] * inv;
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), po,
-                                                 (r * D + 16 * t + 4 * lq) * 4, 0, kSc1);
-        }
-        return;
+      for (int t = 0; t < TMD; ++t) {
+        f32x4 o = oacc[t] * inv;
+        *reinterpret_cast<f32x4*>(dst + 16 * t + 4 * lq) = o;
       }
-      dst = a.part_o + prow * D;
-      if (lq == 0) a.part_lse[prow] = lse_nat;
+      return;
     }
+    // Partials: written through the XCD's L2 (cache policy sc1), which the kernel's end then
+    // need not write back (measured: a launch storing 8 MiB ends ~0.6 us sooner; the 40-layer
+    // step, whose window layers store theirs for the merge inside the launch, ran ~5 us
+    // faster).  Buffer bases are this (KV head, split)'s block of rows.
+    const int64_t blk = ((int64_t)g * a.num_splits + s) * rows;
+    const __amdgpu_buffer_rsrc_t po =
+        __builtin_amdgcn_make_buffer_rsrc(a.part_o + blk * D, 0, rows * D * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t pl =
+        __builtin_amdgcn_make_buffer_rsrc(a.part_lse + blk, 0, rows * 4, 0x00020000);
+    if (lq == 0)
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse_nat), pl, r * 4, 0,
+                                            kSc1);
 #pragma unroll
     for (int t = 0; t < TMD; ++t) {
       f32x4 o = oacc[t] * inv;
-      *reinterpret_cast<f32x4*>(dst + 16 * t + 4 * lq) = o;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), po,
+                                             (r * D + 16 * t + 4 * lq) * 4, 0, kSc1);
     }
   };
   if constexpr (!FUSE) {
