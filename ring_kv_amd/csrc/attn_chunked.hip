@@ -20,8 +20,8 @@
 //
 // A ring layer can run as one launch (FUSE): the split workgroups of each (KV head, row tile)
 // are placed on one XCD, store their partials, wait for each other through a counter in the
-// workspace, and each merges a share of the tile's rows from that XCD's L2; otherwise a second
-// launch merges the partials (attn_merge.hip), with the same bits.
+// workspace, and each merges a share of the tile's rows; otherwise a second launch merges the
+// partials (attn_merge.hip), with the same bits.
 //
 // Memory path: K and V chunks stream from HBM with 16-byte loads (a wave reads 1 KiB contiguous
 // per instruction) two chunks ahead of the compute, staged in registers and written into two
@@ -121,8 +121,9 @@ constexpr int kSc1 = 16;
 // order), so both paths give the same bits.  Each pass takes RPP rows, D/4 threads per row, each
 // owning four output dimensions, so a wave instruction reads whole 4*D-byte partial rows; the
 // split weights of a row are computed once (one exponential per thread) and shared through
-// LDS.  Loads miss the L1 (cache policy sc0) and find the partials in the XCD's L2.  bad: write
-// NaN instead (a workgroup of the group ran on another XCD, or never arrived).
+// LDS.  Loads miss the L1 (cache policy sc0); the partials, stored through the XCD's L2 and
+// acknowledged before each arrival, come from that L2 or from memory.  bad: write NaN instead
+// (a workgroup of the group ran on another XCD, or never arrived).
 template <int D, int NT, int ROWS>
 __device__ __forceinline__ void merge_share(const ChunkAttnArgs& a, int g, int row0, int s,
                                             bool bad) {
@@ -874,7 +875,7 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
   } else {
     if ((KS == 1 || kh == 0) && wave_active && row_ok) store_rows();
     // ---- the group merges its partials once all of them are stored ---------------------------
-    // A workgroup's stores reach the XCD's L2 (the L1 writes through) once acknowledged; its
+    // A workgroup's partial stores are acknowledged once written through the XCD's L2; its
     // arrival follows every thread's acknowledgement.  The last of the group's S arrivals checks
     // the group and moves the generation; the others wait for it to move (a bounded poll) and
     // then every workgroup merges its share of the tile's rows.  The group's workgroups are all

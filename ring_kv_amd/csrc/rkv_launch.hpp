@@ -76,7 +76,7 @@ constexpr int kVerifyMaxRows = 256;
 constexpr int kPrefillTileRows = 256;
 // The one-launch ring layer: the workgroups of one (KV head, row tile) all run on one XCD; once
 // all of them have stored their partials, each merges a share of the tile's rows, reading the
-// partials from that XCD's L2.  Used for ring splits up to kFuseMaxSplits whose (head, tile)
+// partials through that XCD's L2.  Used for ring splits up to kFuseMaxSplits whose (head, tile)
 // groups divide evenly over the kXcds XCDs and whose grid fits one workgroup per compute unit.
 constexpr int kFuseMaxSplits = 12;
 constexpr int kXcds = 8;
