@@ -43,7 +43,9 @@ sys.path.insert(0, ROOT)
 METRIC = "KV GB/s (% of HBM peak) for 16-token verify attention; µs/layer at 256K"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_chunk_attn_paged_131k.json")
-KERNEL_SRC = os.path.join(ROOT, "ring_kv_amd", "csrc", "attn_chunked.hip")
+# the paged split kernel's source: its file and the two headers it includes
+KERNEL_SRCS = [os.path.join(ROOT, "ring_kv_amd", "csrc", f)
+               for f in ("attn_chunked.hip", "rkv_device.hpp", "rkv_launch.hpp")]
 # timed calls per single-layer workload: 200 for the short ones, 51 (a multiple of the three
 # pool copies) for the 262,144-context layer, the prefill blocks and the paging calls
 N_SMALL, N_LARGE = 200, 51
@@ -79,7 +81,17 @@ def parse():
 
 
 def kernel_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """16 hex digits of the sha256 of the paged split kernel's code: its source files with
+    comments and blank space taken out, so that an edit to a comment keeps the HBM counter
+    record valid and any change to the code drops it."""
+    import re
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        src = open(path, encoding="utf-8").read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
+    return h.hexdigest()[:16]
 
 
 def graph_ms(fn, inner, reps, torch):

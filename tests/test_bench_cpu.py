@@ -77,3 +77,14 @@ def test_step_parity_compares_outputs_and_the_accept():
     p = bench.step_parity(off, ref)
     assert not p["within_tolerance"] and not p["accept_exact"]
     assert abs(p["max_abs_out"] - 0.02) < 1e-5
+
+
+def test_kernel_hash_ignores_comments_only(tmp_path, monkeypatch):
+    src = tmp_path / "k.hip"
+    src.write_text("// head\nint f() { return 1; } /* tail */\n")
+    monkeypatch.setattr(bench, "KERNEL_SRCS", [str(src)])
+    h0 = bench.kernel_hash()
+    src.write_text("// another comment\nint f()  {\n  return 1;   // why\n}\n")
+    assert bench.kernel_hash() == h0
+    src.write_text("int f() { return 2; }\n")
+    assert bench.kernel_hash() != h0
