@@ -6,7 +6,9 @@
 // the parts reduce to the row argmaxes, then the first disagreement with the draft and the
 // committed tokens.  Ties go to the lower index, values compare as float32 (-0 == +0).
 // (A single launch that lets the last workgroup finish needs a device-scope release from
-// every workgroup, which costs more here than the second launch.)
+// every workgroup, which costs more here than the second launch; with the parts written and
+// read by device-coherent stores and loads instead of a release, and an arrival counter, the
+// accept over [17 x 65,536] took 10.7 us against 8.7 us for the two launches.)
 #include <limits.h>
 
 #include "rkv_device.hpp"
