@@ -792,45 +792,59 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
   float l = __shfl(lacc[0], ln, kWave);
   float lfr = row_sum4(lf);
   if constexpr (KS == 2) {
-    // key half 1 hands (m, l, lf, O) to key half 0 through LDS; every chunk load has landed
+    // The two key halves of a row group exchange their states through LDS, and each combines
+    // half of the row's dimensions (wave kh keeps the 16-byte columns t of O in
+    // [kh * TMD/2, (kh + 1) * TMD/2) and hands the other half to its partner); both compute
+    // the row's combined weights from the same values, so they agree bit for bit.  Every chunk
+    // load has landed.
+    constexpr int TH = TMD / 2;
     float* xo = reinterpret_cast<float*>(&lds[0][0]);          // [NRG][16][D]
-    float* xm = xo + NRG * 16 * D;                               // [NRG][16]
-    float* xl = xm + NRG * 16;
-    float* xf = xl + NRG * 16;
-    static_assert((NRG * 16 * D + 3 * NRG * 16) * 4 <= NLDS * T::elems * 2, "exchange fits");
+    float* xm = xo + NRG * 16 * D;                               // [2][NRG][16]
+    float* xl = xm + 2 * NRG * 16;
+    float* xf = xl + 2 * NRG * 16;
+    static_assert((NRG * 16 * D + 6 * NRG * 16) * 4 <= NLDS * T::elems * 2, "exchange fits");
     // row (rg, ln), 16-byte column 4t + lq of D/4, XOR-swizzled by the row so that the 16
     // lanes of one access group (16 rows, same column) land in 16 different bank groups
     auto xo_off = [&](int t) __attribute__((always_inline)) {
       return (rg * 16 + ln) * D + (((4 * t + lq) ^ ln) << 2);
     };
+    const int r16 = rg * 16 + ln;
     lds_barrier();
-    if (kh == 1 && wave_active) {
+    if (wave_active) {
+      if (kh == 0) {
 #pragma unroll
-      for (int t = 0; t < TMD; ++t)
-        *reinterpret_cast<f32x4*>(&xo[xo_off(t)]) = oacc[t];
+        for (int t = TH; t < TMD; ++t) *reinterpret_cast<f32x4*>(&xo[xo_off(t)]) = oacc[t];
+      } else {
+#pragma unroll
+        for (int t = 0; t < TH; ++t) *reinterpret_cast<f32x4*>(&xo[xo_off(t)]) = oacc[t];
+      }
       if (lq == 0) {
-        xm[rg * 16 + ln] = m_run;
-        xl[rg * 16 + ln] = l;
-        xf[rg * 16 + ln] = lfr;
+        xm[kh * NRG * 16 + r16] = m_run;
+        xl[kh * NRG * 16 + r16] = l;
+        xf[kh * NRG * 16 + r16] = lfr;
       }
     }
     lds_barrier();
-    if constexpr (!FUSE) {
-      if (kh == 1) return;
-    }
-    if (kh == 0 && wave_active) {
-      const float m1 = xm[rg * 16 + ln];
-      const float l1 = xl[rg * 16 + ln];
-      const float M = fmaxf(m_run, m1);
+    if (wave_active) {
+      const float m0 = xm[r16], m1 = xm[NRG * 16 + r16];
+      const float M = fmaxf(m0, m1);
       const float Mu = M == -INFINITY ? 0.f : M;
-      const float a0 = __builtin_amdgcn_exp2f(m_run - Mu);
+      const float a0 = __builtin_amdgcn_exp2f(m0 - Mu);
       const float a1 = __builtin_amdgcn_exp2f(m1 - Mu);
-      l = a0 * l + a1 * l1;
-      lfr = a0 * lfr + a1 * xf[rg * 16 + ln];
+      l = a0 * xl[r16] + a1 * xl[NRG * 16 + r16];
+      lfr = a0 * xf[r16] + a1 * xf[NRG * 16 + r16];
+      if (kh == 0) {
 #pragma unroll
-      for (int t = 0; t < TMD; ++t) {
-        const f32x4 o1 = *reinterpret_cast<const f32x4*>(&xo[xo_off(t)]);
-        oacc[t] = oacc[t] * a0 + o1 * a1;
+        for (int t = 0; t < TH; ++t) {
+          const f32x4 o1 = *reinterpret_cast<const f32x4*>(&xo[xo_off(t)]);
+          oacc[t] = oacc[t] * a0 + o1 * a1;
+        }
+      } else {
+#pragma unroll
+        for (int t = TH; t < TMD; ++t) {
+          const f32x4 o0 = *reinterpret_cast<const f32x4*>(&xo[xo_off(t)]);
+          oacc[t] = o0 * a0 + oacc[t] * a1;
+        }
       }
       m_run = M;
     }
@@ -840,13 +854,24 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
     const float inv = pos_bad ? __builtin_nanf("") : (l > 0.f ? 1.f / l : 0.f);
     const float lse_nat = pos_bad ? __builtin_nanf("")
                                   : (lfr > 0.f ? (m_run + log2f(lfr)) * kLn2 : -INFINITY);
+    // with two key halves each stores its half of the columns, the first the lse
+    const int t_lo = KS == 2 ? kh * (TMD / 2) : 0;
+    const bool lse_lane = lq == 0 && (KS == 1 || kh == 0);
     if (a.part_o == nullptr) {
       float* dst = a.out + ((int64_t)qi * a.n_q_heads + hq) * D;
-      if (a.lse != nullptr && lq == 0) a.lse[(int64_t)qi * a.n_q_heads + hq] = lse_nat;
+      if (a.lse != nullptr && lse_lane) a.lse[(int64_t)qi * a.n_q_heads + hq] = lse_nat;
+      auto put = [&](int t) __attribute__((always_inline)) {
+        *reinterpret_cast<f32x4*>(dst + 16 * t + 4 * lq) = oacc[t] * inv;
+      };
+      if (KS == 1) {
 #pragma unroll
-      for (int t = 0; t < TMD; ++t) {
-        f32x4 o = oacc[t] * inv;
-        *reinterpret_cast<f32x4*>(dst + 16 * t + 4 * lq) = o;
+        for (int t = 0; t < TMD; ++t) put(t);
+      } else if (t_lo == 0) {
+#pragma unroll
+        for (int t = 0; t < TMD / 2; ++t) put(t);
+      } else {
+#pragma unroll
+        for (int t = TMD / 2; t < TMD; ++t) put(t);
       }
       return;
     }
@@ -859,21 +884,30 @@ void chunk_attn_kernel(ChunkAttnArgs a) {
         __builtin_amdgcn_make_buffer_rsrc(a.part_o + blk * D, 0, rows * D * 4, 0x00020000);
     const __amdgpu_buffer_rsrc_t pl =
         __builtin_amdgcn_make_buffer_rsrc(a.part_lse + blk, 0, rows * 4, 0x00020000);
-    if (lq == 0)
+    if (lse_lane)
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse_nat), pl, r * 4, 0,
                                             kSc1);
-#pragma unroll
-    for (int t = 0; t < TMD; ++t) {
-      f32x4 o = oacc[t] * inv;
+    auto put = [&](int t) __attribute__((always_inline)) {
+      const f32x4 o = oacc[t] * inv;
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), po,
                                              (r * D + 16 * t + 4 * lq) * 4, 0, kSc1);
+    };
+    if (KS == 1) {
+#pragma unroll
+      for (int t = 0; t < TMD; ++t) put(t);
+    } else if (t_lo == 0) {
+#pragma unroll
+      for (int t = 0; t < TMD / 2; ++t) put(t);
+    } else {
+#pragma unroll
+      for (int t = TMD / 2; t < TMD; ++t) put(t);
     }
   };
   if constexpr (!FUSE) {
     if (!wave_active || !row_ok) return;
     store_rows();
   } else {
-    if ((KS == 1 || kh == 0) && wave_active && row_ok) store_rows();
+    if (wave_active && row_ok) store_rows();
     // ---- the group merges its partials once all of them are stored ---------------------------
     // A workgroup's partial stores are acknowledged once written through the XCD's L2; its
     // arrival follows every thread's acknowledgement.  The last of the group's S arrivals checks
