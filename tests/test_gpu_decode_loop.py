@@ -42,10 +42,13 @@ def _close(got, want, what):
     return err, lerr
 
 
-@pytest.mark.parametrize("fused", [False, True], ids=["append_then_attend", "append_in_attention"])
-def test_one_graph_replayed_over_decode_steps(fused):
+@pytest.mark.parametrize("fused,P0,N", [(False, 9000, 10), (True, 9000, 10), (True, 131000, 4)],
+                         ids=["append_then_attend", "append_in_attention",
+                              "append_in_attention_131k"])
+def test_one_graph_replayed_over_decode_steps(fused, P0, N):
     """Four layers (three window layers over 2,048-slot rings, one full-attention layer over a
-    permuted pool) at a context of 9,000 committed positions; ten decode steps from one graph.
+    permuted pool) at a context of 9,000 committed positions, ten decode steps from one graph;
+    and at 131,000 (the 40-layer step's context) for four steps.
     Each step: the block's 16 K/V rows are appended at the device position in every layer, each
     layer attends, the accept runs over [16 x 4,096] logits with a planted agreement prefix, and
     the position advances by a + 1 on the device.  The block is the last committed token and 15
@@ -56,7 +59,7 @@ def test_one_graph_replayed_over_decode_steps(fused):
     attention launch)."""
     g = np.random.default_rng(2026)
     kinds = ["ring", "ring", "ring", "paged"]
-    P0, N, V = 9000, 10, 4096
+    V = 4096
     pos_cap = P0 + Q * N
     n_table = -(-(pos_cap + Q) // CH)          # every chunk any step can reach, reserved
     n_slots = n_table + 5
@@ -151,8 +154,11 @@ def test_one_graph_replayed_over_decode_steps(fused):
             if kind == "ring":
                 host[i] = list(oracle.append_ring(*host[i], s["kn"][i], s["vn"][i], P))
                 want = oracle.attention_ring(s["q"][i], *host[i], P, P % R, R, W)
-                plain = oracle.attention_contiguous(s["q"][i], hk, hv, P + Q, window=W,
-                                                    dtype="bf16")
+                # the same window over the history from the first key any query sees (the
+                # positions shift together, the window's keys stay the same)
+                lo = max(0, P - W + 1)
+                plain = oracle.attention_contiguous(s["q"][i], hk[lo:], hv[lo:], P + Q - lo,
+                                                    window=W, dtype="bf16")
             else:
                 host[i] = list(oracle.append_paged(*host[i], pt, s["kn"][i], s["vn"][i], P))
                 want = oracle.attention_paged(s["q"][i], *host[i], pt, P + Q)
